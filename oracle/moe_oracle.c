@@ -129,13 +129,13 @@ int oracle_int4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t r
 
 /* ------------------------------------------------------------------ a1: router logits (R1) */
 
-/* The fp64 dot product in wave-64 order. */
-static double dot_wave64(const void* x, int x_dt, int64_t xoff, const float* w, int64_t woff, int H) {
+/* The fp64 dot product of two rows (already widened to double) in wave-64 order. */
+static double dot_wave64(const double* a, const double* b, int H) {
     double P[64];
     for (int j = 0; j < 64; j++) P[j] = 0.0;
     for (int base = 0; base < H; base += 64)
         for (int j = 0; j < 64 && base + j < H; j++)
-            P[j] += act_value(x, x_dt, xoff + base + j) * (double)w[woff + base + j];
+            P[j] += a[base + j] * b[base + j];          /* exact product; one rounding per add */
     for (int step = 32; step >= 1; step >>= 1)
         for (int j = 0; j < step; j++) P[j] += P[j + step];
     return P[0];
@@ -146,12 +146,20 @@ static double dot_wave64(const void* x, int x_dt, int64_t xoff, const float* w, 
 int oracle_router_logits(const void* x, int x_dt, const float* Wr, const float* bias,
                          int64_t T, int H, int E, float* logits) {
     if (!x || !Wr || !logits || T < 0 || H <= 0 || E <= 0) return OR_EINVAL;
-    for (int64_t t = 0; t < T; t++)
+    double* w = (double*)malloc(sizeof(double) * (size_t)E * (size_t)H);
+    double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!w || !xr) { free(w); free(xr); return OR_ENOMEM; }
+    for (int64_t i = 0; i < (int64_t)E * H; i++) w[i] = (double)Wr[i];
+    for (int64_t t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) xr[h] = act_value(x, x_dt, t * (int64_t)H + h);
         for (int e = 0; e < E; e++) {
-            float l = (float)dot_wave64(x, x_dt, t * (int64_t)H, Wr, (int64_t)e * H, H);
+            float l = (float)dot_wave64(xr, w + (int64_t)e * H, H);
             if (bias) l = l + bias[e];          /* fp32 add, no contraction */
             logits[t * E + e] = l;
         }
+    }
+    free(w);
+    free(xr);
     return OR_OK;
 }
 
@@ -226,10 +234,13 @@ int oracle_expert_ffn(const void* x, int x_dt, int64_t xoff,
                       int e, int H, int F, int round_a_bf16, double* y) {
     double* a = (double*)malloc(sizeof(double) * (size_t)F);
     if (!a) return OR_ENOMEM;
+    double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!xr) { free(a); return OR_ENOMEM; }
+    for (int h = 0; h < H; h++) xr[h] = act_value(x, x_dt, xoff + h);
     for (int f = 0; f < F; f++) {
         double g = 0.0, u = 0.0;
         for (int h = 0; h < H; h++) {
-            double xv = act_value(x, x_dt, xoff + h);
+            double xv = xr[h];
             g += xv * weight_value(wg, sg, w_dt, e, F, H, f, h);
             u += xv * weight_value(wu, su, w_dt, e, F, H, f, h);
         }
@@ -243,6 +254,7 @@ int oracle_expert_ffn(const void* x, int x_dt, int64_t xoff,
         y[h] = acc;
     }
     free(a);
+    free(xr);
     return OR_OK;
 }
 
