@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the routed-expert (sparse mixture-of-experts) layer for
+ * AMD MI355X (gfx950).  Library: routed_expert_ffn_amd/_lib/libmoe.so.
+ *
+ * The operation, per the pages this library follows:
+ *   "Strata Coder 编程模型深度剖析：RCO 专家剪枝砍掉一半专家却保留 91% 编程能力",
+ *     §1 "先搞懂 Strata": a 48-layer model of 512 experts per layer in which the
+ *        router picks 10 experts for every token;
+ *     §3 "RCO 专家剪枝是怎么砍一半而不伤脑的": every expert has gate, up and down
+ *        matrices; pruning counts which experts the routing selects on
+ *        calibration data and keeps the 256 most-selected of each layer, with one
+ *        keep decision for all three matrices, the kept experts listed in their
+ *        original order.
+ *   Coder benchmark write-up (kwkr.cn), "测试环境与运行配置": still 10 active
+ *     experts per token after pruning; prefill in chunks of up to 8,192 tokens;
+ *     speculative verify of 4 drafted tokens plus one.
+ * The expert is the SwiGLU y = Wd (silu(Wg x) * (Wu x)); routing weights are the
+ * softmax over the K selected logits; ties go to the lower expert id.
+ *
+ * Conventions for every call:
+ *   - All tensors are row-major and contiguous.  Every pointer argument is a
+ *     DEVICE pointer owned by the caller (the library allocates nothing and
+ *     keeps no per-call state); only sizes and enums are host values.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it: no host synchronisation, no device->host copies.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error the outputs are untouched and nothing is launched.
+ *       MOE_ERR_INVALID_ARG  null required pointer, non-positive size, K > E,
+ *                            counts that overflow int32, unknown dtype;
+ *       MOE_ERR_UNSUPPORTED  a valid request this build does not implement
+ *                            (listed per call), or a pointer not aligned to 16 B;
+ *       MOE_ERR_WORKSPACE    workspace smaller than the matching *_workspace_size;
+ *       MOE_ERR_HIP          a kernel launch reported an error.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Calls are re-entrant; calls on different streams may run concurrently
+ *     if their buffers do not overlap.
+ *   - bf16 tensors are passed as 16-bit bit patterns; int4 weights as packed
+ *     bytes (see MOE_INT4_B32).
+ */
+#ifndef ROUTED_EXPERT_FFN_MOE_H
+#define ROUTED_EXPERT_FFN_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    /* Symmetric int4 in blocks of 32 consecutive elements along the input
+     * (reduction) dimension of each out x in weight row: the element is
+     * d * (nibble - 8), d the block's IEEE fp16 scale; byte j of a row holds
+     * element 2j in its low nibble and 2j+1 in its high nibble. */
+    MOE_INT4_B32 = 2
+} moe_dtype;
+
+typedef void* moe_stream; /* hipStream_t */
+
+/* One layer's expert weights, E experts of width F over hidden size H.
+ *   F32 / BF16:  w_gate, w_up [E][F][H];  w_down [E][H][F];  s_* must be NULL.
+ *   INT4_B32:    w_gate, w_up [E][F][H/2] bytes, s_gate, s_up [E][F][H/32] fp16;
+ *                w_down [E][H][F/2] bytes, s_down [E][H][F/32] fp16. */
+typedef struct {
+    int32_t dtype; /* moe_dtype */
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    const void* s_gate;
+    const void* s_up;
+    const void* s_down;
+} moe_expert_weights;
+
+int moe_abi_version(void);
+const char* moe_status_string(moe_status s);
+
+/* ---------------------------------------------------------------- routing
+ * Router projection, selection and weights (page 1 §1: each token is routed
+ * to K of the E experts).
+ *   x          [T][H] activations, x_dtype MOE_F32 or MOE_BF16.
+ *   w_router   [E][H] fp32.
+ *   bias       [E] fp32 added to every logit (a router offset), or NULL.
+ *   topk_idx   [T][K] int32 out: the K largest logits, in descending order,
+ *              ties to the lower expert id.
+ *   topk_w     [T][K] fp32 out: exp(l_k - l_0) / sum_j exp(l_j - l_0) over the
+ *              K selected.
+ *   logits_out [T][E] fp32 out, or NULL.
+ * Logits are fp32(S + 0) then + bias in fp32, S the fp64 sum of the exact
+ * products x*w taken in wave-64 order (64 strided partial sums, then a pairwise
+ * tree 32,16,...,1); the selection is exact with respect to these values.  A
+ * faster fp32 estimate is used where every gap among the leading K+1 logits
+ * clears a safety margin; other tokens are re-decided on the exact values.
+ * Unsupported: K > 32, E > 4096, H % 8 != 0.  NaN logits give unspecified
+ * selections. */
+size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype);
+moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias,
+                     int32_t T, int32_t H, int32_t E, int32_t K,
+                     int32_t* topk_idx, float* topk_w, float* logits_out,
+                     void* workspace, size_t ws_bytes, moe_stream stream);
+
+/* ---------------------------------------------------------------- grouping
+ * Token->expert grouping: a stable counting sort of the flat slots
+ * s = t*K + k by expert id.
+ *   counts   [E]     int32 out: slots per expert.
+ *   offsets  [E+1]   int32 out: exclusive scan of counts (offsets[E] = T*K).
+ *   perm     [T*K]   int32 out: perm[p] = slot at permuted position p; within an
+ *                    expert's segment slots ascend.
+ *   inv_perm [T*K]   int32 out: inv_perm[perm[p]] = p.
+ * Unsupported: E > 4096. */
+size_t moe_permute_workspace_size(int32_t T, int32_t K, int32_t E);
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                       void* workspace, size_t ws_bytes, moe_stream stream);
+
+/* ---------------------------------------------------------------- experts
+ * Grouped SwiGLU expert FFN (page 1 §3: gate, up and down per expert).  For
+ * every permuted row p in expert e's segment [offsets[e], offsets[e+1]), with
+ * token t = perm[p] / K:
+ *     a = silu(Wg[e] x[t]) * (Wu[e] x[t])      (rounded to bf16 if x is bf16)
+ *     y_perm[p] = Wd[e] a                      (fp32 accumulation)
+ *   x        [T][H] activations, MOE_F32 or MOE_BF16.
+ *   y_perm   [T*K][H] out, y_dtype MOE_F32 or MOE_BF16.
+ * Built combinations: (x F32, weights F32, y F32), (x BF16, weights BF16,
+ * y BF16 or F32), (x BF16, weights INT4_B32, y BF16 or F32).
+ * Unsupported: H or F not a multiple of 64. */
+size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_t F, int32_t x_dtype,
+                              int32_t w_dtype);
+moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w,
+                   const int32_t* offsets, const int32_t* perm,
+                   int32_t T, int32_t K, int32_t H, int32_t F, int32_t E,
+                   void* y_perm, int32_t y_dtype,
+                   void* workspace, size_t ws_bytes, moe_stream stream);
+
+/* ---------------------------------------------------------------- combine
+ *   out[t] = cast( sum_k topk_w[t][k] * y_perm[inv_perm[t*K+k]] + residual[t] )
+ * accumulated in fp32 in k order (a gather: deterministic), one final
+ * rounding to out_dtype (bf16: nearest-even).  residual [T][H] in out_dtype, or
+ * NULL.  out may alias residual (in-place residual update). */
+moe_status moe_combine(const void* y_perm, int32_t y_dtype, const int32_t* inv_perm,
+                       const float* topk_w, const void* residual,
+                       int32_t T, int32_t K, int32_t H, void* out, int32_t out_dtype,
+                       moe_stream stream);
+
+/* ---------------------------------------------------------------- pruning statistic
+ * Per-(layer, expert) selection counts over given router logits (page 1 §3:
+ * routing counted on calibration data, the most-selected kept per layer, kept
+ * experts listed in original order).
+ *   logits   [L][T][E] fp32; each row's top-K follows moe_route's rule.
+ *   counts   [L][E] int64: overwritten (accumulate = 0) or added to
+ *            (accumulate = 1, chunked calibration).
+ *   keep     0: counts only.  Else rank_of [L][E] int32 = position of e in
+ *            (count descending, id ascending) order, and keep_map [L][keep]
+ *            int32 = the ids with rank_of < keep, ascending.
+ * Unsupported: K > 32, E > 4096. */
+moe_status moe_expert_freq(const float* logits, int32_t L, int64_t T, int32_t E, int32_t K,
+                           int64_t* counts, int32_t accumulate, int32_t keep,
+                           int32_t* rank_of, int32_t* keep_map, moe_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROUTED_EXPERT_FFN_MOE_H */

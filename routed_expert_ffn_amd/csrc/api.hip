@@ -1,0 +1,160 @@
+// api.hip -- the C ABI of libmoe (declared in include/moe.h): argument
+// checks, workspace sizing, path selection and kernel launches.  Nothing here
+// allocates memory or synchronises; every call only enqueues on `stream`.
+#include "../../include/moe.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int MAX_E = 4096;
+constexpr int MAX_K = 32;
+constexpr int FAST_ROUTE_MIN_T = 64;      // below this the exact logits are cheap enough
+constexpr float ROUTE_TAU = 1.0f / 4096;  // safety margin of the fp32 logit estimate
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+hipStream_t S(moe_stream s) { return (hipStream_t)s; }
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+__global__ void k_fill_i32(int32_t* p, int n, int v) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+bool fast_route_eligible(int T, int H, int x_dtype, const void* x, const float* logits_out) {
+    return x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && H % 32 == 0 && logits_out == nullptr && aligned16(x);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported request";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+// Workspace: [T][E] fp32 logits, then one int32 counter of re-decided tokens.
+size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype) {
+    (void)H; (void)K; (void)x_dtype;
+    if (T < 0 || E <= 0) return 0;
+    return round256((size_t)T * E * sizeof(float)) + 256;
+}
+
+moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T, int32_t H,
+                     int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
+                     size_t ws_bytes, moe_stream stream) {
+    if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || H <= 0 || E <= 0 || K <= 0 || K > E) return MOE_ERR_INVALID_ARG;
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T * K > INT32_MAX || (int64_t)T * E > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
+    if (K > MAX_K || E > MAX_E || H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe_route_workspace_size(T, H, E, K, x_dtype);
+    if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    hipStream_t st = S(stream);
+    float* lg = (float*)workspace;
+    int32_t* counter = (int32_t*)((char*)workspace + round256((size_t)T * E * sizeof(float)));
+    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, st, counter, 1, 0);
+    const int xb = x_dtype == MOE_BF16;
+    hipError_t err;
+    if (fast_route_eligible(T, H, x_dtype, x, logits_out)) {
+        err = launch_logits_fast((const uint16_t*)x, w_router, bias, T, H, E, lg, st);
+        if (err != hipSuccess) return MOE_ERR_HIP;
+        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, topk_idx, topk_w, counter, st);
+    } else {
+        float* dst = logits_out ? logits_out : lg;
+        err = launch_logits_exact(x, xb, w_router, bias, T, H, E, dst, st);
+        if (err != hipSuccess) return MOE_ERR_HIP;
+        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, topk_idx, topk_w, counter, st);
+    }
+    return hip_status(err);
+}
+
+size_t moe_permute_workspace_size(int32_t T, int32_t K, int32_t E) {
+    if (T < 0 || K <= 0 || E <= 0) return 0;
+    const int64_t n = (int64_t)T * K;
+    if (n <= PERM_CHUNK) return 256;
+    const int64_t chunks = (n + PERM_CHUNK - 1) / PERM_CHUNK;
+    return round256((size_t)chunks * E * sizeof(int32_t));
+}
+
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes, moe_stream stream) {
+    if (!topk_idx || !counts || !offsets || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || K <= 0 || E <= 0 || (int64_t)T * K > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (E > MAX_E) return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe_permute_workspace_size(T, K, E);
+    if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_permute(topk_idx, T * K, E, counts, offsets, perm, inv_perm, (int32_t*)workspace,
+                                     S(stream)));
+}
+
+size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_t F, int32_t x_dtype,
+                              int32_t w_dtype) {
+    if (T < 0 || K <= 0 || E <= 0 || H <= 0 || F <= 0) return 0;
+    return ffn_workspace_bytes(T, K, E, H, F, x_dtype, w_dtype) + 256;
+}
+
+moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, const int32_t* offsets,
+                   const int32_t* perm, int32_t T, int32_t K, int32_t H, int32_t F, int32_t E, void* y_perm,
+                   int32_t y_dtype, void* workspace, size_t ws_bytes, moe_stream stream) {
+    if (!x || !w || !offsets || !perm || !y_perm) return MOE_ERR_INVALID_ARG;
+    if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || K <= 0 || E <= 0 || H <= 0 || F <= 0 || K > E || (int64_t)T * K > INT32_MAX)
+        return MOE_ERR_INVALID_ARG;
+    if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (y_dtype != MOE_F32 && y_dtype != MOE_BF16) ||
+        (w->dtype != MOE_F32 && w->dtype != MOE_BF16 && w->dtype != MOE_INT4_B32))
+        return MOE_ERR_INVALID_ARG;
+    if (w->dtype == MOE_INT4_B32 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T * K * H > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
+    // built combinations
+    if (x_dtype == MOE_F32) {
+        if (w->dtype != MOE_F32 || y_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    } else {
+        if (w->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+        if (H % 128 != 0 || F % 64 != 0) return MOE_ERR_UNSUPPORTED;
+        if (!aligned16(x) || !aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down) ||
+            !aligned16(y_perm))
+            return MOE_ERR_UNSUPPORTED;
+    }
+    const size_t need = moe_ffn_workspace_size(T, K, E, H, F, x_dtype, w->dtype);
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_ffn(x, x_dtype, w->dtype, w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down,
+                                 offsets, perm, T, K, H, F, E, y_perm, y_dtype, workspace, S(stream)));
+}
+
+moe_status moe_combine(const void* y_perm, int32_t y_dtype, const int32_t* inv_perm, const float* topk_w,
+                       const void* residual, int32_t T, int32_t K, int32_t H, void* out, int32_t out_dtype,
+                       moe_stream stream) {
+    if (!y_perm || !inv_perm || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || K <= 0 || H <= 0 || (int64_t)T * K > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+        return MOE_ERR_INVALID_ARG;
+    if (H % 8 != 0 || !aligned16(y_perm) || !aligned16(residual) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_combine(y_perm, y_dtype == MOE_BF16, inv_perm, topk_w, residual, T, K, H, out,
+                                     out_dtype == MOE_BF16, S(stream)));
+}
+
+moe_status moe_expert_freq(const float* logits, int32_t L, int64_t T, int32_t E, int32_t K, int64_t* counts,
+                           int32_t accumulate, int32_t keep, int32_t* rank_of, int32_t* keep_map,
+                           moe_stream stream) {
+    if (!counts || L <= 0 || T < 0 || E <= 0 || K <= 0 || K > E || keep < 0 || keep > E) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && !logits) return MOE_ERR_INVALID_ARG;
+    if (keep > 0 && (!rank_of || !keep_map)) return MOE_ERR_INVALID_ARG;
+    if (L > 65535) return MOE_ERR_INVALID_ARG;
+    if (K > MAX_K || E > MAX_E) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_freq(logits, L, T, E, K, (unsigned long long*)counts, accumulate != 0, keep, rank_of,
+                                  keep_map, S(stream)));
+}
+
+}  // extern "C"

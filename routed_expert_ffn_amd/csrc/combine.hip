@@ -1,0 +1,75 @@
+// combine.hip -- weighted combine of the K expert outputs of each token (gfx950).
+//
+//   out[t] = cast( sum_k w[t][k] * y_perm[inv[t*K + k]] + residual[t] )
+//
+// A gather in k order with fp32 accumulation: no atomics, so the result is
+// deterministic.  Each thread owns 8 consecutive hidden elements (16-byte
+// bf16 loads/stores); the residual add (between stacked MoE layers) is fused
+// before the single rounding.
+#include "common.h"
+#include "launch.h"
+
+template <int YB, int OB>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int32_t* __restrict__ inv,
+                                                 const float* __restrict__ w, const void* __restrict__ res, int K,
+                                                 int H, void* __restrict__ out) {
+    const int t = blockIdx.y;
+    const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (h >= H) return;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = 0.f;
+    for (int k = 0; k < K; k++) {
+        const float wk = w[(long)t * K + k];
+        const long row = inv[(long)t * K + k];
+        float v[8];
+        if constexpr (YB) {
+            const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)y + row * H + h);
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) { v[2 * i] = bf16lo_to_f32(u[i]); v[2 * i + 1] = bf16hi_to_f32(u[i]); }
+        } else {
+            const float4 a = *reinterpret_cast<const float4*>((const float*)y + row * H + h);
+            const float4 b = *reinterpret_cast<const float4*>((const float*)y + row * H + h + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] = fmaf(wk, v[i], acc[i]);
+    }
+    const long o = (long)t * H + h;
+    if (res) {
+        if constexpr (OB) {
+            const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)res + o);
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) { acc[2 * i] += bf16lo_to_f32(u[i]); acc[2 * i + 1] += bf16hi_to_f32(u[i]); }
+        } else {
+            const float4 a = *reinterpret_cast<const float4*>((const float*)res + o);
+            const float4 b = *reinterpret_cast<const float4*>((const float*)res + o + 4);
+            acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+            acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+        }
+    }
+    if constexpr (OB) {
+        uint4 q;
+        q.x = pack_bf16x2(acc[0], acc[1]);
+        q.y = pack_bf16x2(acc[2], acc[3]);
+        q.z = pack_bf16x2(acc[4], acc[5]);
+        q.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>((uint16_t*)out + o) = q;
+    } else {
+        *reinterpret_cast<float4*>((float*)out + o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>((float*)out + o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
+hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w, const void* res, int T,
+                          int K, int H, void* out, int out_bf16, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    dim3 grid((H + 2047) / 2048, T);
+    if (y_bf16 && out_bf16) hipLaunchKernelGGL((k_combine<1, 1>), grid, dim3(256), 0, st, y, inv, w, res, K, H, out);
+    else if (y_bf16) hipLaunchKernelGGL((k_combine<1, 0>), grid, dim3(256), 0, st, y, inv, w, res, K, H, out);
+    else if (out_bf16) hipLaunchKernelGGL((k_combine<0, 1>), grid, dim3(256), 0, st, y, inv, w, res, K, H, out);
+    else hipLaunchKernelGGL((k_combine<0, 0>), grid, dim3(256), 0, st, y, inv, w, res, K, H, out);
+    return hipGetLastError();
+}

@@ -1,0 +1,33 @@
+// launch.h -- internal host-side launchers of libmoe's kernels (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// route.hip
+hipError_t launch_logits_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
+                               float* logits, hipStream_t st);
+hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
+                              float* logits, hipStream_t st);
+hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
+                               int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
+                               int32_t* n_rechecked, hipStream_t st);
+
+// permute.hip
+constexpr int PERM_CHUNK = 2048;   // slots per grouping block
+hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, int32_t* chunk_buf, hipStream_t st);
+
+// ffn.hip
+size_t ffn_workspace_bytes(int T, int K, int E, int H, int F, int x_dtype, int w_dtype);
+hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, const void* wu, const void* wd,
+                      const void* sg, const void* su, const void* sd, const int32_t* offsets, const int32_t* perm,
+                      int T, int K, int H, int F, int E, void* y, int y_dtype, void* ws, hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w, const void* res, int T,
+                          int K, int H, void* out, int out_bf16, hipStream_t st);
+
+// freq.hip
+hipError_t launch_freq(const float* logits, int L, int64_t T, int E, int K, unsigned long long* counts,
+                       int accumulate, int keep, int32_t* rank_of, int32_t* keep_map, hipStream_t st);
