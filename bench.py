@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+One step = one pass of the whole hot path (route -> permute -> ffn ->
+combine) over one batch of synthetic input.  The headline workload is the
+speculative verify step: 5 tokens (4 drafted + 1, the pages' `--spec 4`),
+hidden 2048, 512 experts, top-10, expert width 512, bf16 weights, fp32 router.
+Further workloads (the 8192-token prefill chunk, the pruning statistic over
+48 x 262144 x 512 logits, the pruned 48-layer int4 stack) are reported under
+"also".
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workloads verify,prefill,freq,stack]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "routed tokens/s per MoE layer (8192-tok prefill; 5-tok verify); % HBM/MFMA peak"
+N_SETS = 8                     # rotating weight sets: 8 x 3.2 GB defeats the 256 MB MALL
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "routed_expert_ffn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_sha):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not d or d.get("src_sha") != src_sha:
+        return None
+    return d.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the current stream, bracketed by device synchronisation."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, reps):
+        torch = self.torch
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return s.elapsed_time(e) / 1e3, wall
+
+
+def capture(torch, fn):
+    """Capture fn() (a sequence of library calls on the current stream) in a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                       # warm: allocations and lazy init happen outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+# ------------------------------------------------------------------ verify / prefill layers
+def layer_bytes_and_flops(s, counts_list, expert_bytes):
+    """Algorithmic HBM bytes and flops of one layer step, from the run's actual routing."""
+    n = s.T * s.K
+    out = []
+    for counts in counts_list:
+        touched = int((counts > 0).sum())
+        b_router = s.E * s.H * 4 + s.T * s.H * 2 + s.T * s.K * 8
+        b_ffn = touched * expert_bytes + s.T * s.H * 2 + n * s.F * 2 * 2 + n * s.H * 2
+        b_comb = n * s.H * 2 + s.T * s.H * 2 + s.T * s.K * 8
+        f_router = 2.0 * s.T * s.H * s.E
+        f_ffn = 2.0 * n * 3 * s.H * s.F
+        out.append(dict(touched=touched, b_router=b_router, b_ffn=b_ffn, b_step=b_router + b_ffn + b_comb,
+                        f_router=f_router, f_ffn=f_ffn))
+    return out
+
+
+def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph, name):
+    dev = torch.device("cuda:0")
+    log(f"[{name}] generating {sets} weight set(s) of {shape}")
+    layers = [synth.make_device_layer(shape, seed=0, cfg=cfg_id, layer=i, device=dev) for i in range(sets)]
+    x = layers[0].x
+    for L in layers[1:]:
+        L.x = x
+    torch.cuda.synchronize()
+    wdt = {"bf16": moe.BF16, "int4": moe.INT4_B32}[shape.wdt]
+    lw = moe.LayerWorkspace(shape.T, shape.H, shape.E, shape.K, shape.F, x_dtype=x.dtype, w_dtype=wdt)
+
+    def step(L):
+        return moe.layer(L.x, L.wr, L.wg, L.wu, L.wd, shape.K, bias=L.bias, sg=L.sg, su=L.su, sd=L.sd, lw=lw)
+
+    # per-set routing (for the algorithmic byte counts and the per-call timings)
+    per_set = []
+    for L in layers:
+        _, r = step(L)
+        per_set.append({k: v.clone() for k, v in r.items() if k != "y"})
+    torch.cuda.synchronize()
+    counts = [p["counts"].cpu().numpy() for p in per_set]
+    acct = layer_bytes_and_flops(shape, counts, synth.expert_bytes(shape))
+
+    def all_sets():
+        for L in layers:
+            step(L)
+
+    timer = Timer(torch)
+    reps = max(1, -(-steps // sets))
+    wreps = max(1, -(-warmup // sets))
+    if use_graph:
+        g = capture(torch, all_sets)
+        fn = g.replay
+    else:
+        fn = all_sets
+    timer.run(fn, wreps)
+    dt, wall = timer.run(fn, reps)
+    n_steps = reps * sets
+    ms = dt / n_steps * 1e3
+    # per-call breakdown (each call captured alone over the rotating sets)
+    y = lw.y
+    ws_r, ws_p, ws_f = lw.route_ws, lw.perm_ws, lw.ffn_ws
+
+    def calls_route():
+        for L in layers:
+            moe.route(L.x, L.wr, shape.K, bias=L.bias, workspace=ws_r, out=lw.route_out)
+
+    def calls_permute():
+        for p in per_set:
+            moe.permute(p["idx"], shape.E, workspace=ws_p, out=lw.perm_out)
+
+    def calls_ffn():
+        for L, p in zip(layers, per_set):
+            moe.ffn(L.x, L.wg, L.wu, L.wd, p["offsets"], p["perm"], shape.K, L.sg, L.su, L.sd, out=y, workspace=ws_f)
+
+    def calls_combine():
+        for p in per_set:
+            moe.combine(y, p["inv"], p["w"], out=lw.out)
+
+    parts = {}
+    for pname, f in (("route", calls_route), ("permute", calls_permute), ("ffn", calls_ffn),
+                     ("combine", calls_combine)):
+        gf = capture(torch, f).replay if use_graph else f
+        timer.run(gf, wreps)
+        t, _ = timer.run(gf, reps)
+        parts[pname] = t / n_steps * 1e6
+    b_step = sum(a["b_step"] for a in acct) / len(acct)
+    b_ffn = sum(a["b_ffn"] for a in acct) / len(acct)
+    f_ffn = acct[0]["f_ffn"]
+    f_all = acct[0]["f_ffn"] + acct[0]["f_router"]
+    touched = sum(a["touched"] for a in acct) / len(acct)
+    res = dict(name=name, T=shape.T, ms_per_step=ms, value=shape.T / (ms / 1e3), steps=n_steps, warmup=wreps * sets,
+               wall_s=wall, parts_us=parts, touched_experts=touched, bytes_per_step=b_step, bytes_ffn=b_ffn,
+               flops_ffn=f_ffn, flops_step=f_all,
+               hbm_frac_step=b_step / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
+               mfma_frac_step=f_all / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
+               mfma_frac_experts=f_ffn / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12))
+    t_ffn = parts["ffn"] / 1e6
+    res["ffn_hbm_gbs"] = b_ffn / t_ffn / 1e9
+    res["ffn_tflops"] = f_ffn / t_ffn / 1e12
+    del layers, lw
+    return res
+
+
+def roofline_for(res, bound, kernel_key, src_sha):
+    t = res["parts_us"]["ffn"] / 1e6
+    if bound == "hbm":
+        a = res["bytes_ffn"] / t / 1e9
+        return dict(bound="hbm", achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(a / HBM_PEAK_GBS, 4),
+                    traffic=measured_traffic(kernel_key, src_sha), kernel="moe_ffn (gate/up + down launches)",
+                    algorithmic_bytes_per_launch=int(res["bytes_ffn"]), launch_us=round(res["parts_us"]["ffn"], 2))
+    a = res["flops_ffn"] / t / 1e12
+    return dict(bound="mfma", achieved=round(a, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(a / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic(kernel_key, src_sha),
+                kernel="moe_ffn (gate/up + down launches)", algorithmic_flops_per_launch=res["flops_ffn"],
+                launch_us=round(res["parts_us"]["ffn"], 2))
+
+
+# ------------------------------------------------------------------ pruning statistic
+def bench_freq(torch, moe, synth, steps, warmup, use_graph):
+    L, T, E, K, keep = synth.FREQ_L, synth.FREQ_T, synth.FREQ_E, synth.FREQ_K, synth.FREQ_KEEP
+    log(f"[freq] generating {L} x {T} x {E} fp32 logits")
+    lg = torch.empty((L, T, E), dtype=torch.float32, device="cuda")
+    for l in range(L):
+        synth.make_device_logits_layer(T, E, seed=0, cfg=4, layer=l, device="cuda", out=lg[l])
+    counts = torch.zeros((L, E), dtype=torch.int64, device="cuda")
+    rank_of = torch.empty((L, E), dtype=torch.int32, device="cuda")
+    keep_map = torch.empty((L, keep), dtype=torch.int32, device="cuda")
+    lib = moe.load()
+
+    def step():
+        rc = lib.moe_expert_freq(moe._ptr(lg), L, T, E, K, moe._ptr(counts), 0, keep, moe._ptr(rank_of),
+                                 moe._ptr(keep_map), moe._stream())
+        assert rc == 0
+    timer = Timer(torch)
+    fn = capture(torch, step).replay if use_graph else step
+    timer.run(fn, max(1, warmup))
+    n = max(3, steps)
+    dt, wall = timer.run(fn, n)
+    ms = dt / n * 1e3
+    nbytes = L * T * E * 4 + L * E * 8 * 2
+    a = nbytes / (ms / 1e3) / 1e9
+    res = dict(name="pruning statistic 48x262144x512 fp32 logits, top-10, keep 256", ms_per_step=ms,
+               value=L * T / (ms / 1e3), unit="logit rows/s", steps=n, wall_s=wall,
+               roofline=dict(bound="hbm", achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(a / HBM_PEAK_GBS, 4), kernel="moe_expert_freq",
+                             traffic=measured_traffic("freq", src_hash("freq.hip"))))
+    del lg
+    return res
+
+
+# ------------------------------------------------------------------ pruned 48-layer int4 stack
+def bench_stack(torch, moe, synth, shape, steps, warmup, use_graph, name):
+    Ls = synth.STACK_INT4_LAYERS
+    log(f"[{name}] generating {Ls} int4 layers")
+    layers = [synth.make_device_layer(shape, seed=0, cfg=5, layer=l, device="cuda") for l in range(Ls)]
+    x0 = layers[0].x
+    torch.cuda.synchronize()
+    lw = moe.LayerWorkspace(shape.T, shape.H, shape.E, shape.K, shape.F, x_dtype=torch.bfloat16, w_dtype=moe.INT4_B32)
+    h = torch.empty_like(x0)
+
+    def step():
+        h.copy_(x0)
+        for L in layers:
+            moe.layer(h, L.wr, L.wg, L.wu, L.wd, shape.K, sg=L.sg, su=L.su, sd=L.sd, residual=h, lw=lw, out=h)
+    timer = Timer(torch)
+    fn = capture(torch, step).replay if use_graph else step
+    timer.run(fn, max(1, warmup))
+    n = max(2, steps)
+    dt, wall = timer.run(fn, n)
+    ms = dt / n * 1e3
+    res = dict(name=name, T=shape.T, layers=Ls, ms_per_step=ms, ms_per_layer=ms / Ls,
+               value=shape.T * Ls / (ms / 1e3), unit="tokens/s per MoE layer (48-layer stack)", steps=n, wall_s=wall)
+    del layers
+    return res
+
+
+# ------------------------------------------------------------------ CPU baseline (the oracle)
+def cpu_baseline_verify(torch, synth, budget_s=12.0):
+    import numpy as np
+
+    import oracle
+    s = synth.VERIFY_BF16
+    d = synth.make_device_layer(s, seed=0, cfg=2, layer=0, device="cuda")
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731  (bf16 -> raw bits)
+    x, wr = bits(d.x), d.wr.cpu().numpy()
+    W = oracle.Weights("bf16", bits(d.wg), bits(d.wu), bits(d.wd))
+    del d
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        idx, w, _ = oracle.route(x, wr, s.K)
+        oracle.permute(idx, s.E)
+        oracle.layer_rows(x, idx, w, W)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    return dict(value=round(s.T * reps / el, 3), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"the full 5-token verify step (route, permute, 10 experts per token, combine) of weight set 0, "
+                       f"repeated {reps} times ({el:.1f} s, single-threaded C, fp64)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workloads", default="verify,prefill,freq,stack")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches instead of HIP graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the MoE layer is not sharded across GPUs in this build "
+              "(token rows shard with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from routed_expert_ffn_amd import moe, synth
+    moe.load()
+    use_graph = not args.no_graph
+    wl = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    also = []
+    main_res = None
+    if "verify" in wl:
+        main_res = bench_layer(torch, moe, synth, synth.VERIFY_BF16, 2, args.steps, args.warmup, N_SETS, use_graph,
+                               "verify step 5 tok, E512 top-10 bf16")
+        log(f"[verify] {main_res['ms_per_step']*1e3:.1f} us/step  parts {main_res['parts_us']}")
+    if "prefill" in wl:
+        r = bench_layer(torch, moe, synth, synth.PREFILL_BF16, 3, max(8, args.steps // 10), 8, 1, use_graph,
+                        "prefill chunk 8192 tok, E512 top-10 bf16, Zipf(1.1) router offset")
+        r["roofline"] = roofline_for(r, "mfma", "ffn_prefill", src_hash("ffn.hip"))
+        r["unit"] = "tokens/s"
+        log(f"[prefill] {r['ms_per_step']:.3f} ms/step  parts {r['parts_us']}")
+        also.append(r)
+        torch.cuda.empty_cache()
+    if "freq" in wl:
+        r = bench_freq(torch, moe, synth, max(5, args.steps // 20), 2, use_graph)
+        log(f"[freq] {r['ms_per_step']:.3f} ms/step")
+        also.append(r)
+        torch.cuda.empty_cache()
+    if "stack" in wl:
+        for shp, nm in ((synth.STACK_INT4_VERIFY, "pruned 48-layer int4 stack, 5-tok verify"),
+                        (synth.STACK_INT4_PREFILL, "pruned 48-layer int4 stack, 8192-tok prefill")):
+            r = bench_stack(torch, moe, synth, shp, max(3, args.steps // 40), 1, use_graph, nm)
+            log(f"[stack T={shp.T}] {r['ms_per_step']:.3f} ms/step")
+            also.append(r)
+            torch.cuda.empty_cache()
+
+    if main_res is None:          # a partial run (e.g. under a profiler): report the first workload
+        main_res = also.pop(0) if also else None
+        if main_res is None:
+            sys.exit("no workload ran")
+    cpu = None
+    if not args.no_cpu_baseline and main_res.get("T") == 5 and "verify" in main_res["name"]:
+        cpu = cpu_baseline_verify(torch, synth)
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["value"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": main_res["steps"],
+        "warmup": main_res.get("warmup", args.warmup),
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": main_res["name"], "tokens": main_res.get("T"), "hidden": 2048, "experts": 512,
+                   "top_k": 10, "expert_width": 512, "weight_sets_rotated": N_SETS if "verify" in main_res["name"] else 1,
+                   "hip_graph": use_graph},
+        "roofline": roofline_for(main_res, "hbm", "ffn_verify", src_hash("ffn.hip")) if "verify" in main_res["name"]
+        else main_res.get("roofline"),
+        "cpu_baseline": cpu,
+        "step_breakdown_us": {k: round(v, 2) for k, v in main_res.get("parts_us", {}).items()},
+        "step_hbm_frac": round(main_res.get("hbm_frac_step", 0.0), 4),
+        "also": also,
+    }
+    print(json.dumps(line, default=lambda o: round(o, 4) if isinstance(o, float) else str(o)))
+
+
+if __name__ == "__main__":
+    main()

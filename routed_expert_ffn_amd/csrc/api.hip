@@ -53,8 +53,8 @@ size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int3
 moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T, int32_t H,
                      int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
                      size_t ws_bytes, moe_stream stream) {
-    if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
     if (T < 0 || H <= 0 || E <= 0 || K <= 0 || K > E) return MOE_ERR_INVALID_ARG;
+    if (!w_router || (T > 0 && (!x || !topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
     if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if ((int64_t)T * K > INT32_MAX || (int64_t)T * E > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
     if (K > MAX_K || E > MAX_E || H % 8 != 0) return MOE_ERR_UNSUPPORTED;
@@ -90,8 +90,8 @@ size_t moe_permute_workspace_size(int32_t T, int32_t K, int32_t E) {
 
 moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes, moe_stream stream) {
-    if (!topk_idx || !counts || !offsets || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
     if (T < 0 || K <= 0 || E <= 0 || (int64_t)T * K > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (!counts || !offsets || (T > 0 && (!topk_idx || !perm || !inv_perm))) return MOE_ERR_INVALID_ARG;
     if (E > MAX_E) return MOE_ERR_UNSUPPORTED;
     const size_t need = moe_permute_workspace_size(T, K, E);
     if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -108,10 +108,10 @@ size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_
 moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, const int32_t* offsets,
                    const int32_t* perm, int32_t T, int32_t K, int32_t H, int32_t F, int32_t E, void* y_perm,
                    int32_t y_dtype, void* workspace, size_t ws_bytes, moe_stream stream) {
-    if (!x || !w || !offsets || !perm || !y_perm) return MOE_ERR_INVALID_ARG;
-    if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
     if (T < 0 || K <= 0 || E <= 0 || H <= 0 || F <= 0 || K > E || (int64_t)T * K > INT32_MAX)
         return MOE_ERR_INVALID_ARG;
+    if (!w || !offsets || (T > 0 && (!x || !perm || !y_perm))) return MOE_ERR_INVALID_ARG;
+    if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
     if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (y_dtype != MOE_F32 && y_dtype != MOE_BF16) ||
         (w->dtype != MOE_F32 && w->dtype != MOE_BF16 && w->dtype != MOE_INT4_B32))
         return MOE_ERR_INVALID_ARG;
@@ -136,8 +136,8 @@ moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, 
 moe_status moe_combine(const void* y_perm, int32_t y_dtype, const int32_t* inv_perm, const float* topk_w,
                        const void* residual, int32_t T, int32_t K, int32_t H, void* out, int32_t out_dtype,
                        moe_stream stream) {
-    if (!y_perm || !inv_perm || !topk_w || !out) return MOE_ERR_INVALID_ARG;
     if (T < 0 || K <= 0 || H <= 0 || (int64_t)T * K > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!y_perm || !inv_perm || !topk_w || !out)) return MOE_ERR_INVALID_ARG;
     if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
         return MOE_ERR_INVALID_ARG;
     if (H % 8 != 0 || !aligned16(y_perm) || !aligned16(residual) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;

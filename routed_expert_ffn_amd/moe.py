@@ -130,8 +130,8 @@ def route_workspace_size(T, H, E, K, x_dtype=BF16) -> int:
     return int(load().moe_route_workspace_size(T, H, E, K, x_dtype))
 
 
-def route(x, w_router, K: int, bias=None, logits_out=None, workspace=None, stream=None):
-    """Top-K expert ids [T][K] int32 and weights [T][K] fp32."""
+def route(x, w_router, K: int, bias=None, logits_out=None, workspace=None, stream=None, out=None):
+    """Top-K expert ids [T][K] int32 and weights [T][K] fp32 (out: optional (idx, w) to fill)."""
     _need(x, "x")
     T, H = x.shape
     E = w_router.shape[0]
@@ -140,8 +140,13 @@ def route(x, w_router, K: int, bias=None, logits_out=None, workspace=None, strea
         _need(bias, "bias", torch.float32, (E,))
     if logits_out is not None:
         _need(logits_out, "logits_out", torch.float32, (T, E))
-    idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
-    w = torch.empty((T, K), dtype=torch.float32, device=x.device)
+    if out is not None:
+        idx, w = out
+        _need(idx, "topk_idx", torch.int32, (T, K))
+        _need(w, "topk_w", torch.float32, (T, K))
+    else:
+        idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, K), dtype=torch.float32, device=x.device)
     nb = route_workspace_size(T, H, E, K, _act_dtype(x))
     ws = _workspace(nb, x.device, workspace)
     _chk(load().moe_route(_ptr(x), _act_dtype(x), _ptr(w_router), _ptr(bias), T, H, E, K, _ptr(idx), _ptr(w),
@@ -154,15 +159,21 @@ def permute_workspace_size(T, K, E) -> int:
     return int(load().moe_permute_workspace_size(T, K, E))
 
 
-def permute(topk_idx, E: int, workspace=None, stream=None):
-    """(counts [E], offsets [E+1], perm [T*K], inv_perm [T*K]), all int32."""
+def permute(topk_idx, E: int, workspace=None, stream=None, out=None):
+    """(counts [E], offsets [E+1], perm [T*K], inv_perm [T*K]), all int32 (out: optional tuple to fill)."""
     _need(topk_idx, "topk_idx", torch.int32)
     T, K = topk_idx.shape
     dev = topk_idx.device
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(T * K, dtype=torch.int32, device=dev)
-    inv = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if out is not None:
+        counts, offsets, perm, inv = out
+        for n, t, shp in (("counts", counts, (E,)), ("offsets", offsets, (E + 1,)), ("perm", perm, (T * K,)),
+                          ("inv_perm", inv, (T * K,))):
+            _need(t, n, torch.int32, shp)
+    else:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        perm = torch.empty(T * K, dtype=torch.int32, device=dev)
+        inv = torch.empty(T * K, dtype=torch.int32, device=dev)
     nb = permute_workspace_size(T, K, E)
     ws = _workspace(nb, dev, workspace)
     _chk(load().moe_permute(_ptr(topk_idx), T, K, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws),
@@ -262,6 +273,11 @@ class LayerWorkspace:
         self.perm_ws = torch.empty(permute_workspace_size(T, K, E), dtype=torch.uint8, device=device)
         self.ffn_ws = torch.empty(ffn_workspace_size(T, K, E, H, F, xd, w_dtype), dtype=torch.uint8, device=device)
         self.y = torch.empty((T * K, H), dtype=self.y_dtype, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.route_out = (torch.empty((T, K), **i32), torch.empty((T, K), dtype=torch.float32, device=device))
+        self.perm_out = (torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(T * K, **i32),
+                         torch.empty(T * K, **i32))
+        self.out = torch.empty((T, H), dtype=x_dtype, device=device)
 
 
 def layer(x, w_router, wg, wu, wd, K: int, bias=None, sg=None, su=None, sd=None, residual=None, lw=None,
@@ -269,9 +285,13 @@ def layer(x, w_router, wg, wu, wd, K: int, bias=None, sg=None, su=None, sd=None,
     """route -> permute -> ffn -> combine for one MoE layer.  Returns (out, routing dict)."""
     T, H = x.shape
     E, F = wg.shape[0], wg.shape[1]
-    idx, w = route(x, w_router, K, bias=bias, workspace=lw.route_ws if lw else None, stream=stream)
-    counts, offsets, perm, inv = permute(idx, E, workspace=lw.perm_ws if lw else None, stream=stream)
+    idx, w = route(x, w_router, K, bias=bias, workspace=lw.route_ws if lw else None, stream=stream,
+                   out=lw.route_out if lw else None)
+    counts, offsets, perm, inv = permute(idx, E, workspace=lw.perm_ws if lw else None, stream=stream,
+                                         out=lw.perm_out if lw else None)
     y = ffn(x, wg, wu, wd, offsets, perm, K, sg, su, sd, y_dtype=lw.y_dtype if lw else None,
             out=lw.y if lw else None, workspace=lw.ffn_ws if lw else None, stream=stream)
+    if out is None and lw is not None:
+        out = lw.out
     o = combine(y, inv, w, residual=residual, out_dtype=x.dtype, out=out, stream=stream)
     return o, dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, y=y)
