@@ -17,11 +17,6 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 hipStream_t S(moe_stream s) { return (hipStream_t)s; }
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-__global__ void k_fill_i32(int32_t* p, int n, int v) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
 bool fast_route_eligible(int T, int H, int x_dtype, const void* x, const float* logits_out) {
     return x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && H % 32 == 0 && logits_out == nullptr && aligned16(x);
 }
@@ -43,11 +38,11 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-// Workspace: [T][E] fp32 logits, then one int32 counter of re-decided tokens.
+// Workspace: [T][E] fp32 logits, then [T] int32 flags (1 = token re-decided on exact logits).
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype) {
     (void)H; (void)K; (void)x_dtype;
     if (T < 0 || E <= 0) return 0;
-    return round256((size_t)T * E * sizeof(float)) + 256;
+    return round256((size_t)T * E * sizeof(float)) + round256((size_t)T * sizeof(int32_t)) + 256;
 }
 
 moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T, int32_t H,
@@ -63,19 +58,18 @@ moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, cons
     if (T == 0) return MOE_OK;
     hipStream_t st = S(stream);
     float* lg = (float*)workspace;
-    int32_t* counter = (int32_t*)((char*)workspace + round256((size_t)T * E * sizeof(float)));
-    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, st, counter, 1, 0);
+    int32_t* flags = (int32_t*)((char*)workspace + round256((size_t)T * E * sizeof(float)));
     const int xb = x_dtype == MOE_BF16;
     hipError_t err;
     if (fast_route_eligible(T, H, x_dtype, x, logits_out)) {
         err = launch_logits_fast((const uint16_t*)x, w_router, bias, T, H, E, lg, st);
         if (err != hipSuccess) return MOE_ERR_HIP;
-        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, topk_idx, topk_w, counter, st);
+        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, topk_idx, topk_w, flags, st);
     } else {
         float* dst = logits_out ? logits_out : lg;
         err = launch_logits_exact(x, xb, w_router, bias, T, H, E, dst, st);
         if (err != hipSuccess) return MOE_ERR_HIP;
-        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, topk_idx, topk_w, counter, st);
+        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, topk_idx, topk_w, flags, st);
     }
     return hip_status(err);
 }

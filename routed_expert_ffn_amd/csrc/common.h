@@ -69,6 +69,31 @@ MOE_DEV void wave_best(float& v, int& i) {
     }
 }
 
+// Routing order as one 64-bit key: larger value first, then lower index.
+// The float maps to an order-preserving unsigned (-0 and +0 compare equal, as
+// in IEEE comparison); the low word is the complemented index.
+MOE_DEV uint32_t f32_order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV unsigned long long route_key(float v, int idx) {
+    return ((unsigned long long)f32_order_key(v) << 32) | (uint32_t)(~(uint32_t)idx);
+}
+MOE_DEV int route_key_index(unsigned long long k) { return (int)(~(uint32_t)k); }
+MOE_DEV float route_key_value(unsigned long long k) {
+    const uint32_t h = (uint32_t)(k >> 32);
+    return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
+}
+MOE_DEV unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const unsigned long long o = __shfl_xor(k, d, WAVE);
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // The tile that block `bid` of a grouped launch works on: experts own

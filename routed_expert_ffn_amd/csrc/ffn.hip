@@ -355,6 +355,9 @@ hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, c
                            offsets, n, H, F, E, (float*)y);
         return hipGetLastError();
     }
+    if (ffn_small_eligible(T, H, F))
+        return launch_ffn_small(x, w_dtype, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y,
+                                y_dtype == DT_BF16, ws, st);
     uint16_t* abuf = (uint16_t*)ws;
     const int tiles_g = (n + G_BM - 1) / G_BM + (E < n ? E : n);
     const int tiles_d = (n + D_BM - 1) / D_BM + (E < n ? E : n);

@@ -183,46 +183,57 @@ __global__ __launch_bounds__(256) void k_logits_fast(const uint16_t* __restrict_
 
 constexpr int SEL_CAP = 64;   // candidates re-decided on exact logits (one per lane)
 
+// Top-`rounds` keys of the lane-strided values v[j] (e = lane + 64 j); lane r
+// receives round r's key.  Selected entries are cleared from k[].
+template <int VPL>
+MOE_DEV unsigned long long select_rounds(unsigned long long (&k)[VPL], int rounds) {
+    const int l = lane_id();
+    unsigned long long mine = 0;
+    for (int r = 0; r < rounds; r++) {
+        unsigned long long b = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; j++) b = k[j] > b ? k[j] : b;
+        b = wave_max_u64(b);
+        const int idx = route_key_index(b);
+        if ((idx & (WAVE - 1)) == l) {
+#pragma unroll
+            for (int j = 0; j < VPL; j++)
+                if (j == (idx >> 6)) k[j] = 0;
+        }
+        if (l == r) mine = b;
+    }
+    return mine;
+}
+
 template <int VPL, typename XT>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ logits, int T, int E, int K,
                                                       float tau, int exact,
                                                       const XT* __restrict__ x, const float* __restrict__ wr,
                                                       const float* __restrict__ bias, int H,
                                                       int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                                      int32_t* __restrict__ n_rechecked) {
+                                                      int32_t* __restrict__ rechecked) {
     const int wave = threadIdx.x / WAVE;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int l = lane_id();
     const float* row = logits + (long)t * E;
-    const float NEG = -__builtin_inff();
 
     float v[VPL];
+    unsigned long long k[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; j++) {
         const int e = l + j * WAVE;
-        v[j] = (e < E) ? row[e] : NEG;
+        v[j] = e < E ? row[e] : 0.f;
+        k[j] = e < E ? route_key(v[j], e) : 0ull;
     }
-    unsigned long long taken = 0;
     const int rounds = (exact || K == E) ? K : K + 1;
-    float sel_v = NEG;   // lane r < rounds keeps round r's (value, index)
-    int sel_i = 0x7FFFFFFF;
-    for (int r = 0; r < rounds; r++) {
-        float bv = NEG;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int j = 0; j < VPL; j++) {
-            const int e = l + j * WAVE;
-            if (e < E && !((taken >> j) & 1ull) && key_better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
-        }
-        wave_best(bv, bi);
-        if ((bi & (WAVE - 1)) == l) taken |= 1ull << (bi / WAVE);
-        if (l == r) { sel_v = bv; sel_i = bi; }
-    }
+    unsigned long long sel = select_rounds<VPL>(k, rounds);
+    float sel_v = route_key_value(sel);
+    int sel_i = route_key_index(sel);
 
     bool flagged = false;
     if (!exact) {
-        // gaps between consecutive selected values (and the (K+1)-th, if any)
+        // every gap between consecutive selected values, down to the (K+1)-th, must clear tau
         const float nxt = __shfl_down(sel_v, 1, WAVE);
         const bool check = l < K && l + 1 < rounds;
         flagged = __ballot(check && !(sel_v - nxt >= tau)) != 0;
@@ -230,8 +241,7 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
 
     if (flagged) {
         // Candidates: every expert whose estimate exceeds the K-th estimate - tau.
-        const float vk = __shfl(sel_v, K - 1, WAVE);
-        const float cut = vk - tau;
+        const float cut = __shfl(sel_v, K - 1, WAVE) - tau;
         int ncand = 0;
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
@@ -239,9 +249,8 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
             ncand += wave_sum((e < E && v[j] > cut) ? 1 : 0);
         }
         const XT* xrow = x + (long)t * H;
-        float cv = NEG;
-        int ci = 0x7FFFFFFF;
         if (ncand <= SEL_CAP) {
+            unsigned long long ck = 0;      // lane c holds candidate c's exact key
             int slot = 0;
 #pragma unroll
             for (int j = 0; j < VPL; j++) {
@@ -253,66 +262,117 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
                     const int ce = src + j * WAVE;
                     float lv = (float)wave_dot_exact(xrow, wr + (long)ce * H, H);
                     if (bias) lv = __fadd_rn(lv, bias[ce]);
-                    if (l == slot) { cv = lv; ci = ce; }
+                    if (l == slot) ck = route_key(lv, ce);
                     slot++;
                 }
             }
-            // top-K among the candidates (one per lane)
-            unsigned long long ctaken = 0;
-            for (int r = 0; r < K; r++) {
-                float bv = ((ctaken >> l) & 1ull) ? NEG : cv;
-                int bi = ((ctaken >> l) & 1ull) ? 0x7FFFFFFF : ci;
-                wave_best(bv, bi);
-                ctaken |= __ballot(ci == bi);
-                if (l == r) { sel_v = bv; sel_i = bi; }
-            }
+            unsigned long long c1[1] = {ck};
+            sel = select_rounds<1>(c1, K);
         } else {
             // too many near-equal estimates: decide on exact logits of all experts
-            float ev[VPL];
+            unsigned long long ek[VPL];
 #pragma unroll
             for (int j = 0; j < VPL; j++) {
-                ev[j] = NEG;
+                ek[j] = 0;
                 for (int src = 0; src < WAVE; src++) {
                     const int ce = src + j * WAVE;
                     if (ce >= E) break;
                     float lv = (float)wave_dot_exact(xrow, wr + (long)ce * H, H);
                     if (bias) lv = __fadd_rn(lv, bias[ce]);
-                    if (l == src) ev[j] = lv;
+                    if (l == src) ek[j] = route_key(lv, ce);
                 }
             }
-            unsigned long long tk = 0;
-            for (int r = 0; r < K; r++) {
-                float bv = NEG;
-                int bi = 0x7FFFFFFF;
-#pragma unroll
-                for (int j = 0; j < VPL; j++) {
-                    const int e = l + j * WAVE;
-                    if (e < E && !((tk >> j) & 1ull) && key_better(ev[j], e, bv, bi)) { bv = ev[j]; bi = e; }
-                }
-                wave_best(bv, bi);
-                if ((bi & (WAVE - 1)) == l) tk |= 1ull << (bi / WAVE);
-                if (l == r) { sel_v = bv; sel_i = bi; }
-            }
+            sel = select_rounds<VPL>(ek, K);
         }
-        if (l == 0 && n_rechecked) atomicAdd(n_rechecked, 1);
+        sel_v = route_key_value(sel);
+        sel_i = route_key_index(sel);
     }
+    if (rechecked && l == 0) rechecked[t] = flagged ? 1 : 0;
 
     // weights: softmax over the K selected values
     const float v0 = __shfl(sel_v, 0, WAVE);
     const float ex = (l < K) ? expf(sel_v - v0) : 0.0f;
-    float s = ex;
+    float sum = ex;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, WAVE);
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
     if (l < K) {
         idx_out[(long)t * K + l] = sel_i;
-        w_out[(long)t * K + l] = ex / s;
+        w_out[(long)t * K + l] = ex / sum;
+    }
+}
+
+// ------------------------------------------------------------------ exact logits, few tokens
+
+// One wave per expert, every token: the router row (H fp32) is loaded once into
+// registers (H/64 independent loads per lane in flight); token rows are staged
+// in LDS.  Two experts per block.
+constexpr int XS_MAX_T = 16;
+constexpr int XS_MAX_HL = 64;     // H / 64 values per lane (H <= 4096)
+
+template <typename XT, int HL>
+__global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict__ x, const float* __restrict__ wr,
+                                                            const float* __restrict__ bias, int T, int H, int E,
+                                                            float* __restrict__ logits) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    XT* xs = reinterpret_cast<XT*>(smem);
+    const int tid = threadIdx.x;
+    // stage x [T][H] (16-byte copies)
+    const int per = 16 / (int)sizeof(XT);
+    const int nchunk = T * H / per;
+    for (int i = tid; i < nchunk; i += blockDim.x)
+        reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    __syncthreads();
+    const int e = blockIdx.x * 2 + tid / WAVE;
+    if (e >= E) return;
+    const int l = lane_id();
+    double w[HL];
+#pragma unroll
+    for (int i = 0; i < HL; i++) w[i] = (l + i * WAVE < H) ? (double)wr[(long)e * H + l + i * WAVE] : 0.0;
+    const float b = bias ? bias[e] : 0.f;
+    for (int t = 0; t < T; t++) {
+        double p = 0.0;
+#pragma unroll
+        for (int i = 0; i < HL; i++)
+            if (l + i * WAVE < H) p = __fma_rn(xval(xs + t * H, l + i * WAVE), w[i], p);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) p += __shfl_xor(p, d, WAVE);
+        if (l == 0) {
+            float v = (float)p;
+            if (bias) v = __fadd_rn(v, b);
+            logits[(long)t * E + e] = v;
+        }
     }
 }
 
 // ------------------------------------------------------------------ launchers
 
+template <int HL>
+static bool small_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
+                        float* logits, hipStream_t st) {
+    const size_t lds = (size_t)T * H * (x_bf16 ? 2 : 4);
+    if (x_bf16)
+        hipLaunchKernelGGL((k_logits_exact_small<uint16_t, HL>), dim3((E + 1) / 2), dim3(128), lds, st,
+                           (const uint16_t*)x, wr, bias, T, H, E, logits);
+    else
+        hipLaunchKernelGGL((k_logits_exact_small<float, HL>), dim3((E + 1) / 2), dim3(128), lds, st, (const float*)x,
+                           wr, bias, T, H, E, logits);
+    return true;
+}
+
 hipError_t launch_logits_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
                                float* logits, hipStream_t st) {
+    // few tokens, H a multiple of 64 and 16-byte rows: router rows held in registers
+    if (T <= XS_MAX_T && H % 64 == 0 && H <= 64 * XS_MAX_HL && ((uintptr_t)x & 15) == 0 &&
+        (size_t)T * H * (x_bf16 ? 2 : 4) <= 64 * 1024) {
+        const int hl = H / 64;
+        if (hl == 4) small_exact<4>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else if (hl == 32) small_exact<32>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else if (hl <= 8) small_exact<8>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else if (hl <= 16) small_exact<16>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else if (hl <= 32) small_exact<32>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else small_exact<64>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        return hipGetLastError();
+    }
     const int tpw = T <= 64 ? T : 32;
     dim3 grid((E + 3) / 4, (T + tpw - 1) / tpw);
     if (x_bf16)
@@ -347,13 +407,13 @@ static hipError_t sel_dispatch_x(const float* logits, int T, int E, int K, float
 
 hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
                                int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                               int32_t* n_rechecked, hipStream_t st) {
+                               int32_t* rechecked, hipStream_t st) {
     const int vpl = (E + WAVE - 1) / WAVE;
-    if (vpl <= 1) return sel_dispatch_x<1>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
-    if (vpl <= 2) return sel_dispatch_x<2>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
-    if (vpl <= 4) return sel_dispatch_x<4>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
-    if (vpl <= 8) return sel_dispatch_x<8>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
-    if (vpl <= 16) return sel_dispatch_x<16>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
-    if (vpl <= 32) return sel_dispatch_x<32>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
-    return sel_dispatch_x<64>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, n_rechecked, st);
+    if (vpl <= 1) return sel_dispatch_x<1>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+    if (vpl <= 2) return sel_dispatch_x<2>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+    if (vpl <= 4) return sel_dispatch_x<4>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+    if (vpl <= 8) return sel_dispatch_x<8>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+    if (vpl <= 16) return sel_dispatch_x<16>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+    if (vpl <= 32) return sel_dispatch_x<32>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+    return sel_dispatch_x<64>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
 }

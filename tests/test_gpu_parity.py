@@ -74,6 +74,11 @@ SMALL = [
     synth.LayerShape(T=300, H=256, E=40, K=6, F=128, act="bf16", wdt="int4", zipf=True),
     synth.LayerShape(T=77, H=384, E=100, K=10, F=192, act="bf16", wdt="bf16"),
     synth.LayerShape(T=130, H=128, E=8, K=8, F=64, act="bf16", wdt="int4"),
+    # T <= 16: the weight-streaming path for the verify step
+    synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="bf16", zipf=True),
+    synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="int4", zipf=True),
+    synth.LayerShape(T=3, H=512, E=24, K=8, F=192, act="bf16", wdt="int4"),
+    synth.LayerShape(T=1, H=768, E=300, K=10, F=64, act="bf16", wdt="bf16"),
 ]
 
 
@@ -200,6 +205,18 @@ def test_combine_in_place_residual_and_fp32():
 def test_verify_step_full_size():
     s = synth.VERIFY_BF16
     d = synth.make_device_layer(s, seed=0, cfg=2, layer=0, device="cuda")
+    torch.cuda.synchronize()
+    x, wr = to_host(d.x), to_host(d.wr)
+    ref_idx, ref_w, _ = oracle.route(x, wr, s.K)
+    out, r = run_layer(d)
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    ref_out = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d))
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
+def test_int4_verify_layer_full_size():
+    s = synth.STACK_INT4_VERIFY
+    d = synth.make_device_layer(s, seed=0, cfg=5, layer=0, device="cuda")
     torch.cuda.synchronize()
     x, wr = to_host(d.x), to_host(d.wr)
     ref_idx, ref_w, _ = oracle.route(x, wr, s.K)
