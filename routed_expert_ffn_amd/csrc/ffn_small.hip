@@ -5,7 +5,7 @@
 // gate, up and down matrices are read once, ~1 flop per byte), so the
 // kernels are built for HBM bandwidth, not for MFMA throughput:
 //   * no LDS staging of weights: every lane streams its part of a 16-row
-//     weight tile straight from HBM into registers through an 8-deep ring of
+//     weight tile straight from HBM into registers through a ring of up to 8
 //     16-byte loads, which keeps enough bytes in flight per CU;
 //   * the MFMA 16x16x32 does the dot products (the expert's <= 16 token rows
 //     are the A operand, zero-padded), so no cross-lane reductions are needed;
@@ -29,7 +29,6 @@
 
 enum { SDT_BF16 = 1, SDT_INT4 = 2 };
 constexpr int SM_ROWS = 16;     // rows per expert handled (T <= 16)
-constexpr int SM_RING = 8;      // k steps in flight per lane
 
 MOE_DEV float silu_s(float g) { return g / (1.0f + expf(-g)); }
 
@@ -73,7 +72,7 @@ MOE_DEV uint4 nib8_to_bf16_128(uint32_t w) {
 
 // ---------------------------------------------------------------------------- gate/up
 
-template <int WT>
+template <int WT, int RING>
 __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict__ x, const void* __restrict__ wg_,
                                                       const void* __restrict__ wu_, const uint16_t* __restrict__ sg,
                                                       const uint16_t* __restrict__ su,
@@ -124,24 +123,31 @@ __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict
     if constexpr (WT == SDT_BF16) {
         const uint16_t* pg = (const uint16_t*)wg_ + ((long)e * F + f0 + row) * H + grp * 8;
         const uint16_t* pu = (const uint16_t*)wu_ + ((long)e * F + f0 + row) * H + grp * 8;
-        uint4 rg[SM_RING], ru[SM_RING];
+        uint4 rg[RING], ru[RING];
 #pragma unroll
-        for (int i = 0; i < SM_RING; i++) {
+        for (int i = 0; i < RING; i++) {
             rg[i] = *reinterpret_cast<const uint4*>(pg + i * 32);
             ru[i] = *reinterpret_cast<const uint4*>(pu + i * 32);
         }
-        for (int s0 = 0; s0 < steps; s0 += SM_RING) {
+        // steady state: consume step s, refill its slot with step s + RING (no conditional loads,
+        // so the compiler can wait for the oldest load only)
+        for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
-            for (int i = 0; i < SM_RING; i++) {
+            for (int i = 0; i < RING; i++) {
                 const int s = s0 + i;
                 const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
                 ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rg[i]), ag, 0, 0, 0);
                 au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(ru[i]), au, 0, 0, 0);
-                if (s + SM_RING < steps) {
-                    rg[i] = *reinterpret_cast<const uint4*>(pg + (s + SM_RING) * 32);
-                    ru[i] = *reinterpret_cast<const uint4*>(pu + (s + SM_RING) * 32);
-                }
+                rg[i] = *reinterpret_cast<const uint4*>(pg + (s + RING) * 32);
+                ru[i] = *reinterpret_cast<const uint4*>(pu + (s + RING) * 32);
             }
+        }
+#pragma unroll
+        for (int i = 0; i < RING; i++) {
+            const int s = steps - RING + i;
+            const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rg[i]), ag, 0, 0, 0);
+            au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(ru[i]), au, 0, 0, 0);
         }
     } else {
         // lane: 4 bytes (8 nibbles) of its row per step, plus the row's block scale
@@ -155,39 +161,42 @@ __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict
         const float* xs_r[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) xs_r[r] = xsum + (grp * 4 + r < n ? grp * 4 + r : 0) * nb;
-        uint32_t rg[SM_RING], ru[SM_RING];
-        uint16_t dg[SM_RING], du[SM_RING];
+        uint32_t rg[RING], ru[RING];
+        uint16_t dg[RING], du[RING];
 #pragma unroll
-        for (int i = 0; i < SM_RING; i++) {
+        for (int i = 0; i < RING; i++) {
             rg[i] = pg[i * 4];
             ru[i] = pu[i * 4];
             dg[i] = qg[i];
             du[i] = qu[i];
         }
-        for (int s0 = 0; s0 < steps; s0 += SM_RING) {
+        auto step = [&](int s, uint32_t wgq, uint32_t wuq, uint16_t dgs, uint16_t dus) __attribute__((always_inline)) {
+            const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(wgq)), z, 0, 0, 0);
+            const f32x4_t Du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(wuq)), z, 0, 0, 0);
+            // the scale of this lane's weight row is the scale of its output column (lane & 15)
+            const float dgc = fp16_to_f32(dgs), duc = fp16_to_f32(dus);
 #pragma unroll
-            for (int i = 0; i < SM_RING; i++) {
+            for (int r = 0; r < 4; r++) {
+                const float c = 136.0f * xs_r[r][s];
+                ag[r] = fmaf(dgc, Dg[r] - c, ag[r]);
+                au[r] = fmaf(duc, Du[r] - c, au[r]);
+            }
+        };
+        for (int s0 = 0; s0 < steps - RING; s0 += RING) {
+#pragma unroll
+            for (int i = 0; i < RING; i++) {
                 const int s = s0 + i;
-                const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
-                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4_t Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(rg[i])), z, 0, 0, 0);
-                const f32x4_t Du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(ru[i])), z, 0, 0, 0);
-                // the scale of this lane's weight row is the scale of its output column (lane & 15)
-                const float dgc = fp16_to_f32(dg[i]), duc = fp16_to_f32(du[i]);
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float c = 136.0f * xs_r[r][s];
-                    ag[r] = fmaf(dgc, Dg[r] - c, ag[r]);
-                    au[r] = fmaf(duc, Du[r] - c, au[r]);
-                }
-                if (s + SM_RING < steps) {
-                    rg[i] = pg[(s + SM_RING) * 4];
-                    ru[i] = pu[(s + SM_RING) * 4];
-                    dg[i] = qg[s + SM_RING];
-                    du[i] = qu[s + SM_RING];
-                }
+                step(s, rg[i], ru[i], dg[i], du[i]);
+                rg[i] = pg[(s + RING) * 4];
+                ru[i] = pu[(s + RING) * 4];
+                dg[i] = qg[s + RING];
+                du[i] = qu[s + RING];
             }
         }
+#pragma unroll
+        for (int i = 0; i < RING; i++) step(steps - RING + i, rg[i], ru[i], dg[i], du[i]);
         (void)nb;
     }
     // D[m][c]: lane holds rows m = grp*4 + r, column c = l & 15 (feature f0 + c)
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict
 
 // ---------------------------------------------------------------------------- down
 
-template <int WT, int YBF16>
+template <int WT, int YBF16, int RING>
 __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__ abuf, const void* __restrict__ wd_,
                                                     const uint16_t* __restrict__ sd,
                                                     const int32_t* __restrict__ offsets, int H, int F, int E,
@@ -235,21 +244,26 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
     const bool arow = row < n;
     const uint16_t* ap = abuf + (long)(off + (arow ? row : 0)) * F + grp * 8;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int steps = nb;
     if constexpr (WT == SDT_BF16) {
         const uint16_t* pw = (const uint16_t*)wd_ + ((long)e * H + h0 + row) * F + grp * 8;
-        for (int s0 = 0; s0 < nb; s0 += 16) {
-            uint4 rw[16], ra[16];
+        uint4 rw[RING];
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (s0 + i < nb) rw[i] = *reinterpret_cast<const uint4*>(pw + (s0 + i) * 32);
+        for (int i = 0; i < RING; i++) rw[i] = *reinterpret_cast<const uint4*>(pw + i * 32);
+        for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (s0 + i < nb)
-                    ra[i] = arow ? *reinterpret_cast<const uint4*>(ap + (s0 + i) * 32) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < RING; i++) {
+                const int s = s0 + i;
+                const uint4 av = arow ? *reinterpret_cast<const uint4*>(ap + s * 32) : make_uint4(0, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rw[i]), acc, 0, 0, 0);
+                rw[i] = *reinterpret_cast<const uint4*>(pw + (s + RING) * 32);
+            }
+        }
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (s0 + i < nb)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[i]), as_bf16x8(rw[i]), acc, 0, 0, 0);
+        for (int i = 0; i < RING; i++) {
+            const int s = steps - RING + i;
+            const uint4 av = arow ? *reinterpret_cast<const uint4*>(ap + s * 32) : make_uint4(0, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rw[i]), acc, 0, 0, 0);
         }
     } else {
         const long rowg = (long)e * H + h0 + row;
@@ -258,27 +272,29 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
         const float* as_r[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) as_r[r] = asum + (grp * 4 + r < n ? grp * 4 + r : 0) * nb;
-        for (int s0 = 0; s0 < nb; s0 += 16) {
-            uint32_t rw[16];
-            uint16_t dw[16];
-            uint4 ra[16];
+        uint32_t rw[RING];
+        uint16_t dw[RING];
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (s0 + i < nb) { rw[i] = pw[(s0 + i) * 4]; dw[i] = qd[s0 + i]; }
+        for (int i = 0; i < RING; i++) { rw[i] = pw[i * 4]; dw[i] = qd[i]; }
+        auto step = [&](int s, uint32_t wq, uint16_t ds) __attribute__((always_inline)) {
+            const uint4 av = arow ? *reinterpret_cast<const uint4*>(ap + s * 32) : make_uint4(0, 0, 0, 0);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(wq)), z, 0, 0, 0);
+            const float dc = fp16_to_f32(ds);
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (s0 + i < nb)
-                    ra[i] = arow ? *reinterpret_cast<const uint4*>(ap + (s0 + i) * 32) : make_uint4(0, 0, 0, 0);
+            for (int r = 0; r < 4; r++) acc[r] = fmaf(dc, D[r] - 136.0f * as_r[r][s], acc[r]);
+        };
+        for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (s0 + i < nb) {
-                    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                    const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[i]), as_bf16x8(nib8_to_bf16_128(rw[i])), z, 0, 0, 0);
-                    const float dc = fp16_to_f32(dw[i]);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) acc[r] = fmaf(dc, D[r] - 136.0f * as_r[r][s0 + i], acc[r]);
-                }
+            for (int i = 0; i < RING; i++) {
+                const int s = s0 + i;
+                step(s, rw[i], dw[i]);
+                rw[i] = pw[(s + RING) * 4];
+                dw[i] = qd[s + RING];
+            }
         }
+#pragma unroll
+        for (int i = 0; i < RING; i++) step(steps - RING + i, rw[i], dw[i]);
     }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -293,39 +309,64 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
 
 // ---------------------------------------------------------------------------- host
 
+static int ring_for(int steps) {
+    return steps % 8 == 0 ? 8 : steps % 4 == 0 ? 4 : steps % 2 == 0 ? 2 : 1;
+}
+
 bool ffn_small_eligible(int T, int H, int F) {
-    return T <= SM_ROWS && H % (32 * SM_RING) == 0 && F % 64 == 0 && H % 64 == 0;
+    return T <= SM_ROWS && H % 64 == 0 && F % 64 == 0;
+}
+
+template <int WT, int RG>
+static void gateup_small(dim3 g, size_t lds, hipStream_t st, const void* x, const void* wg, const void* wu,
+                         const void* sg, const void* su, const int32_t* offsets, const int32_t* perm, int K, int H,
+                         int F, int E, int rows_cap, uint16_t* abuf) {
+    hipLaunchKernelGGL((k_gateup_small<WT, RG>), g, dim3(256), lds, st, (const uint16_t*)x, wg, wu,
+                       (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, K, H, F, E, rows_cap, abuf);
+}
+
+template <int WT, int YB, int RG>
+static void down_small(dim3 g, size_t lds, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd,
+                       const int32_t* offsets, int H, int F, int E, void* y) {
+    hipLaunchKernelGGL((k_down_small<WT, YB, RG>), g, dim3(256), lds, st, abuf, wd, (const uint16_t*)sd, offsets, H,
+                       F, E, y);
+}
+
+template <int WT>
+static void launch_wt(const void* x, const void* wg, const void* wu, const void* wd, const void* sg, const void* su,
+                      const void* sd, const int32_t* offsets, const int32_t* perm, int T, int K, int H, int F, int E,
+                      void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
+    const int n = T * K;
+    const int slots = E < n ? E : n;          // at most this many experts are touched
+    const int rows_cap = T < SM_ROWS ? T : SM_ROWS;   // an expert has at most T rows
+    const size_t lds_g = (size_t)rows_cap * (H + 8) * 2 + (WT == SDT_INT4 ? (size_t)rows_cap * (H / 32) * 4 : 0);
+    const size_t lds_d = WT == SDT_INT4 ? (size_t)SM_ROWS * (F / 32) * 4 : 0;
+    dim3 gg(slots, F / 64), gd(slots, H / 64);
+    switch (ring_for(H / 32)) {
+        case 8: gateup_small<WT, 8>(gg, lds_g, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, rows_cap, abuf); break;
+        case 4: gateup_small<WT, 4>(gg, lds_g, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, rows_cap, abuf); break;
+        default: gateup_small<WT, 2>(gg, lds_g, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, rows_cap, abuf); break;
+    }
+    const int rd = ring_for(F / 32);
+    if (y_bf16) {
+        if (rd == 8) down_small<WT, 1, 8>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+        else if (rd == 4) down_small<WT, 1, 4>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+        else down_small<WT, 1, 2>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+    } else {
+        if (rd == 8) down_small<WT, 0, 8>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+        else if (rd == 4) down_small<WT, 0, 4>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+        else down_small<WT, 0, 2>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+    }
 }
 
 hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const void* wu, const void* wd,
                             const void* sg, const void* su, const void* sd, const int32_t* offsets,
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                             hipStream_t st) {
-    const int n = T * K;
-    const int slots = E < n ? E : n;          // at most this many experts are touched
     uint16_t* abuf = (uint16_t*)ws;
-    const int rows_cap = T < SM_ROWS ? T : SM_ROWS;   // an expert has at most T rows
-    const size_t lds_g = (size_t)rows_cap * (H + 8) * 2 + (w_dtype == SDT_INT4 ? (size_t)rows_cap * (H / 32) * 4 : 0);
-    const size_t lds_d = w_dtype == SDT_INT4 ? (size_t)SM_ROWS * (F / 32) * 4 : 0;
-    dim3 gg(slots, (F + 63) / 64), gd(slots, (H + 63) / 64);
-    if (w_dtype == SDT_BF16) {
-        hipLaunchKernelGGL(k_gateup_small<SDT_BF16>, gg, dim3(256), lds_g, st, (const uint16_t*)x, wg, wu, nullptr,
-                           nullptr, offsets, perm, K, H, F, E, rows_cap, abuf);
-        if (y_bf16)
-            hipLaunchKernelGGL((k_down_small<SDT_BF16, 1>), gd, dim3(256), lds_d, st, abuf, wd, nullptr, offsets, H, F,
-                               E, y);
-        else
-            hipLaunchKernelGGL((k_down_small<SDT_BF16, 0>), gd, dim3(256), lds_d, st, abuf, wd, nullptr, offsets, H, F,
-                               E, y);
-    } else {
-        hipLaunchKernelGGL(k_gateup_small<SDT_INT4>, gg, dim3(256), lds_g, st, (const uint16_t*)x, wg, wu,
-                           (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, K, H, F, E, rows_cap, abuf);
-        if (y_bf16)
-            hipLaunchKernelGGL((k_down_small<SDT_INT4, 1>), gd, dim3(256), lds_d, st, abuf, wd, (const uint16_t*)sd,
-                               offsets, H, F, E, y);
-        else
-            hipLaunchKernelGGL((k_down_small<SDT_INT4, 0>), gd, dim3(256), lds_d, st, abuf, wd, (const uint16_t*)sd,
-                               offsets, H, F, E, y);
-    }
+    if (w_dtype == SDT_BF16)
+        launch_wt<SDT_BF16>(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+    else
+        launch_wt<SDT_INT4>(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
     return hipGetLastError();
 }

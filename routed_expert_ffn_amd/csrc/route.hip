@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void k_logits_fast(const uint16_t* __restrict_
 
 constexpr int SEL_CAP = 64;   // candidates re-decided on exact logits (one per lane)
 
-// Top-`rounds` keys of the lane-strided values v[j] (e = lane + 64 j); lane r
-// receives round r's key.  Selected entries are cleared from k[].
+// Top-`rounds` of the keys held by the wave (any layout); lane r receives
+// round r's key.  Selected entries are cleared from k[].
 template <int VPL>
 MOE_DEV unsigned long long select_rounds(unsigned long long (&k)[VPL], int rounds) {
     const int l = lane_id();
@@ -194,12 +194,8 @@ MOE_DEV unsigned long long select_rounds(unsigned long long (&k)[VPL], int round
 #pragma unroll
         for (int j = 0; j < VPL; j++) b = k[j] > b ? k[j] : b;
         b = wave_max_u64(b);
-        const int idx = route_key_index(b);
-        if ((idx & (WAVE - 1)) == l) {
 #pragma unroll
-            for (int j = 0; j < VPL; j++)
-                if (j == (idx >> 6)) k[j] = 0;
-        }
+        for (int j = 0; j < VPL; j++) k[j] = k[j] == b ? 0ull : k[j];   // keys are unique (id embedded)
         if (l == r) mine = b;
     }
     return mine;
@@ -327,13 +323,12 @@ __global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict
     const int l = lane_id();
     double w[HL];
 #pragma unroll
-    for (int i = 0; i < HL; i++) w[i] = (l + i * WAVE < H) ? (double)wr[(long)e * H + l + i * WAVE] : 0.0;
+    for (int i = 0; i < HL; i++) w[i] = (double)wr[(long)e * H + l + i * WAVE];   // H == 64 * HL
     const float b = bias ? bias[e] : 0.f;
     for (int t = 0; t < T; t++) {
         double p = 0.0;
 #pragma unroll
-        for (int i = 0; i < HL; i++)
-            if (l + i * WAVE < H) p = __fma_rn(xval(xs + t * H, l + i * WAVE), w[i], p);
+        for (int i = 0; i < HL; i++) p = __fma_rn(xval(xs + t * H, l + i * WAVE), w[i], p);
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) p += __shfl_xor(p, d, WAVE);
         if (l == 0) {
@@ -361,15 +356,14 @@ static bool small_exact(const void* x, int x_bf16, const float* wr, const float*
 
 hipError_t launch_logits_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
                                float* logits, hipStream_t st) {
-    // few tokens, H a multiple of 64 and 16-byte rows: router rows held in registers
-    if (T <= XS_MAX_T && H % 64 == 0 && H <= 64 * XS_MAX_HL && ((uintptr_t)x & 15) == 0 &&
-        (size_t)T * H * (x_bf16 ? 2 : 4) <= 64 * 1024) {
-        const int hl = H / 64;
+    // few tokens, H = 64 * {4,8,16,32,64} and 16-byte rows: router rows held in registers
+    const int hl = H / 64;
+    if (T <= XS_MAX_T && H % 64 == 0 && (hl == 4 || hl == 8 || hl == 16 || hl == 32 || hl == 64) &&
+        ((uintptr_t)x & 15) == 0 && (size_t)T * H * (x_bf16 ? 2 : 4) <= 64 * 1024) {
         if (hl == 4) small_exact<4>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else if (hl == 8) small_exact<8>(x, x_bf16, wr, bias, T, H, E, logits, st);
+        else if (hl == 16) small_exact<16>(x, x_bf16, wr, bias, T, H, E, logits, st);
         else if (hl == 32) small_exact<32>(x, x_bf16, wr, bias, T, H, E, logits, st);
-        else if (hl <= 8) small_exact<8>(x, x_bf16, wr, bias, T, H, E, logits, st);
-        else if (hl <= 16) small_exact<16>(x, x_bf16, wr, bias, T, H, E, logits, st);
-        else if (hl <= 32) small_exact<32>(x, x_bf16, wr, bias, T, H, E, logits, st);
         else small_exact<64>(x, x_bf16, wr, bias, T, H, E, logits, st);
         return hipGetLastError();
     }
