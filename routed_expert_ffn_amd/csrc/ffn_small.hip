@@ -1,36 +1,48 @@
 // ffn_small.hip -- the expert FFN when every expert has at most 16 rows
-// (T <= 16: the speculative verify step of 4 drafts + 1 and decode).
+// (T <= 16: the speculative verify step of 4 drafts + 1, and decode).
 //
 // Here the layer is a pure stream of expert weights (each touched expert's
-// gate, up and down matrices are read once, ~1 flop per byte), so the
-// kernels are built for HBM bandwidth, not for MFMA throughput:
-//   * no LDS staging of weights: every lane streams its part of a 16-row
-//     weight tile straight from HBM into registers through a ring of up to 8
-//     16-byte loads, which keeps enough bytes in flight per CU;
-//   * the MFMA 16x16x32 does the dot products (the expert's <= 16 token rows
-//     are the A operand, zero-padded), so no cross-lane reductions are needed;
-//   * one block covers one touched expert and 64 output rows (4 waves x 16);
-//     a block finds its expert by a wave-wide scan of the expert offsets, so
+// gate, up and down matrices are read once, ~1 flop per byte), so the kernels
+// are built for HBM bandwidth, not MFMA throughput:
+//   * no LDS staging: every lane streams its part of a 16-row weight tile
+//     straight from HBM into registers (non-temporal 16-byte loads) through a
+//     ring of up to 8 steps; loads are never predicated, so the compiler
+//     waits for the oldest load only;
+//   * the MFMA 16x16x32 does the dot products: the expert's <= 16 token rows
+//     are the A operand (rows past the expert's count read a valid row and
+//     are zeroed), the weight tile is the B operand, no cross-lane reductions;
+//   * gate/up splits K over the 4 waves of a block (each wave a quarter of
+//     H, partial sums added through LDS in a fixed order), so a block is 16
+//     feature rows of gate AND up and the grid has enough blocks to fill all
+//     CUs; down gives each wave 16 hidden rows over the full (short) K = F.
+//   * a block finds its expert by a wave-wide scan of the expert offsets, so
 //     the grid only depends on T*K.
-//
-//   k_gateup_small  a = silu(Wg x) * (Wu x) for 16 feature rows per wave, both
-//                   gate and up streamed together (their epilogue meets in
-//                   registers); x rows staged in LDS; a -> bf16 workspace.
-//   k_down_small    y = Wd a for 16 hidden rows per wave (K = F is short, the
-//                   whole A tile is held in registers).
-// int4 weights: each 32-element block along K is exactly one MFMA K step.  The
-// nibbles become the bf16 values 128 + u (bit pattern 0x4300 | u, exact), so
-// the MFMA gives D = sum x (128 + u); since the weight is d (u - 8),
-//     sum x w = d (D - 136 sum x)
-// with sum x over the block precomputed per row.  The weights enter exactly
-// (no rounding of d*q).
+// int4 weights: each 32-element block along K is one MFMA K step.  The
+// nibbles u become the bf16 values 128 + u (bit pattern 0x4300 | u, exact);
+// with the weight d (u - 8):
+//     sum_k x w = d (D - 136 S),  D = MFMA(x, 128 + u),  S = MFMA(x, 1)
+// so the row sums S come out of the same MFMA layout, and the weights enter
+// exactly (no rounding of d * q).
 #include "common.h"
 #include "launch.h"
 
 enum { SDT_BF16 = 1, SDT_INT4 = 2 };
 constexpr int SM_ROWS = 16;     // rows per expert handled (T <= 16)
+constexpr int GU_SPLIT = 4;     // gate/up: waves per block sharing one 16-row tile, each a quarter of K
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 MOE_DEV float silu_s(float g) { return g / (1.0f + expf(-g)); }
+
+MOE_DEV uint4 ld_nt(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+MOE_DEV uint32_t ld_nt32(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
+MOE_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+MOE_DEV uint4 zero_unless(bool keep, uint4 v) {
+    return keep ? v : make_uint4(0, 0, 0, 0);
+}
 
 // The j-th expert with a non-empty segment (-1 if none); result in every lane.
 MOE_DEV int find_touched(const int32_t* __restrict__ offsets, int E, int j, int& off, int& n) {
@@ -70,6 +82,12 @@ MOE_DEV uint4 nib8_to_bf16_128(uint32_t w) {
     return o;
 }
 
+MOE_DEV uint4 bf16_ones() { return make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u); }
+
+MOE_DEV f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------- gate/up
 
 template <int WT, int RING>
@@ -78,9 +96,9 @@ __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ su,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ perm, int K, int H, int F, int E,
-                                                      int rows_cap, uint16_t* __restrict__ abuf) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+                                                      uint16_t* __restrict__ abuf) {
     __shared__ int s_info[3];
+    __shared__ f32x4_t s_part[GU_SPLIT - 1][2][WAVE];
     const int tid = threadIdx.x;
     if (tid < WAVE) {
         int off = 0, n = 0;
@@ -90,114 +108,102 @@ __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict
     __syncthreads();
     const int e = s_info[0], off = s_info[1], n = s_info[2];
     if (e < 0) return;
-    const int LDX = H + 8;                       // padded row (bank spread)
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    float* xsum = reinterpret_cast<float*>(smem + (size_t)rows_cap * LDX * 2);   // [rows][H/32] (int4 only)
-    // stage the expert's token rows
-    const int chunks = H / 8;
-    for (int i = tid; i < n * chunks; i += blockDim.x) {
-        const int r = i / chunks, c = (i % chunks) * 8;
-        const long t = perm[off + r] / K;
-        *reinterpret_cast<uint4*>(&xs[r * LDX + c]) = *reinterpret_cast<const uint4*>(x + t * H + c);
-    }
-    __syncthreads();
-    if constexpr (WT == SDT_INT4) {
-        const int nb = H / 32;
-        for (int i = tid; i < n * nb; i += blockDim.x) {
-            const int r = i / nb, b = i % nb;
-            float s = 0.f;
-            for (int k = 0; k < 32; k++) s += bf16_to_f32(xs[r * LDX + b * 32 + k]);
-            xsum[r * nb + b] = s;
-        }
-        __syncthreads();
-    }
     const int wave = tid / WAVE, l = lane_id();
-    const int f0 = (blockIdx.y * 4 + wave) * 16;
-    if (f0 >= F) return;
+    const int f0 = blockIdx.y * 16;
     const int row = l & 15, grp = l >> 4;
     const bool arow = row < n;
-    const uint16_t* xa = xs + row * LDX + grp * 8;
-    const int steps = H / 32;
+    const long tok = perm[off + (arow ? row : 0)] / K;
+    const int steps = H / 32 / GU_SPLIT;            // K steps of this wave
+    const int k0 = wave * steps * 32;               // this wave's quarter of H
+    const uint16_t* xa = x + tok * H + k0 + grp * 8;
 
     f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
     if constexpr (WT == SDT_BF16) {
-        const uint16_t* pg = (const uint16_t*)wg_ + ((long)e * F + f0 + row) * H + grp * 8;
-        const uint16_t* pu = (const uint16_t*)wu_ + ((long)e * F + f0 + row) * H + grp * 8;
-        uint4 rg[RING], ru[RING];
+        const uint16_t* pg = (const uint16_t*)wg_ + ((long)e * F + f0 + row) * H + k0 + grp * 8;
+        const uint16_t* pu = (const uint16_t*)wu_ + ((long)e * F + f0 + row) * H + k0 + grp * 8;
+        uint4 rg[RING], ru[RING], rx[RING];
 #pragma unroll
         for (int i = 0; i < RING; i++) {
-            rg[i] = *reinterpret_cast<const uint4*>(pg + i * 32);
-            ru[i] = *reinterpret_cast<const uint4*>(pu + i * 32);
+            rg[i] = ld_nt(pg + i * 32);
+            ru[i] = ld_nt(pu + i * 32);
+            rx[i] = ld16(xa + i * 32);
         }
-        // steady state: consume step s, refill its slot with step s + RING (no conditional loads,
-        // so the compiler can wait for the oldest load only)
         for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
             for (int i = 0; i < RING; i++) {
                 const int s = s0 + i;
-                const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
-                ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rg[i]), ag, 0, 0, 0);
-                au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(ru[i]), au, 0, 0, 0);
-                rg[i] = *reinterpret_cast<const uint4*>(pg + (s + RING) * 32);
-                ru[i] = *reinterpret_cast<const uint4*>(pu + (s + RING) * 32);
+                const uint4 av = zero_unless(arow, rx[i]);
+                ag = mfma(av, rg[i], ag);
+                au = mfma(av, ru[i], au);
+                rg[i] = ld_nt(pg + (s + RING) * 32);
+                ru[i] = ld_nt(pu + (s + RING) * 32);
+                rx[i] = ld16(xa + (s + RING) * 32);
             }
         }
 #pragma unroll
         for (int i = 0; i < RING; i++) {
-            const int s = steps - RING + i;
-            const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
-            ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rg[i]), ag, 0, 0, 0);
-            au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(ru[i]), au, 0, 0, 0);
+            const uint4 av = zero_unless(arow, rx[i]);
+            ag = mfma(av, rg[i], ag);
+            au = mfma(av, ru[i], au);
         }
     } else {
         // lane: 4 bytes (8 nibbles) of its row per step, plus the row's block scale
         const long rowg = (long)e * F + f0 + row;
-        const uint32_t* pg = reinterpret_cast<const uint32_t*>((const uint8_t*)wg_ + rowg * (H / 2) + grp * 4);
-        const uint32_t* pu = reinterpret_cast<const uint32_t*>((const uint8_t*)wu_ + rowg * (H / 2) + grp * 4);
-        const uint16_t* qg = sg + rowg * (H / 32);
-        const uint16_t* qu = su + rowg * (H / 32);
-        const int nb = H / 32;
-        // correction rows: this lane's output rows are (grp*4 + r)
-        const float* xs_r[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) xs_r[r] = xsum + (grp * 4 + r < n ? grp * 4 + r : 0) * nb;
+        const uint8_t* pg = (const uint8_t*)wg_ + rowg * (H / 2) + k0 / 2 + grp * 4;
+        const uint8_t* pu = (const uint8_t*)wu_ + rowg * (H / 2) + k0 / 2 + grp * 4;
+        const uint16_t* qg = sg + rowg * (H / 32) + k0 / 32;
+        const uint16_t* qu = su + rowg * (H / 32) + k0 / 32;
         uint32_t rg[RING], ru[RING];
         uint16_t dg[RING], du[RING];
+        uint4 rx[RING];
 #pragma unroll
         for (int i = 0; i < RING; i++) {
-            rg[i] = pg[i * 4];
-            ru[i] = pu[i * 4];
+            rg[i] = ld_nt32(pg + i * 16);
+            ru[i] = ld_nt32(pu + i * 16);
             dg[i] = qg[i];
             du[i] = qu[i];
+            rx[i] = ld16(xa + i * 32);
         }
-        auto step = [&](int s, uint32_t wgq, uint32_t wuq, uint16_t dgs, uint16_t dus) __attribute__((always_inline)) {
-            const uint4 av = arow ? *reinterpret_cast<const uint4*>(xa + s * 32) : make_uint4(0, 0, 0, 0);
+        auto step = [&](uint4 xv, uint32_t wgq, uint32_t wuq, uint16_t dgs, uint16_t dus) __attribute__((always_inline)) {
+            const uint4 av = zero_unless(arow, xv);
             const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(wgq)), z, 0, 0, 0);
-            const f32x4_t Du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(wuq)), z, 0, 0, 0);
+            const f32x4_t S = mfma(av, bf16_ones(), z);
+            const f32x4_t Dg = mfma(av, nib8_to_bf16_128(wgq), z);
+            const f32x4_t Du = mfma(av, nib8_to_bf16_128(wuq), z);
             // the scale of this lane's weight row is the scale of its output column (lane & 15)
             const float dgc = fp16_to_f32(dgs), duc = fp16_to_f32(dus);
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float c = 136.0f * xs_r[r][s];
-                ag[r] = fmaf(dgc, Dg[r] - c, ag[r]);
-                au[r] = fmaf(duc, Du[r] - c, au[r]);
+                ag[r] = fmaf(dgc, fmaf(-136.0f, S[r], Dg[r]), ag[r]);
+                au[r] = fmaf(duc, fmaf(-136.0f, S[r], Du[r]), au[r]);
             }
         };
         for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
             for (int i = 0; i < RING; i++) {
                 const int s = s0 + i;
-                step(s, rg[i], ru[i], dg[i], du[i]);
-                rg[i] = pg[(s + RING) * 4];
-                ru[i] = pu[(s + RING) * 4];
+                step(rx[i], rg[i], ru[i], dg[i], du[i]);
+                rg[i] = ld_nt32(pg + (s + RING) * 16);
+                ru[i] = ld_nt32(pu + (s + RING) * 16);
                 dg[i] = qg[s + RING];
                 du[i] = qu[s + RING];
+                rx[i] = ld16(xa + (s + RING) * 32);
             }
         }
 #pragma unroll
-        for (int i = 0; i < RING; i++) step(steps - RING + i, rg[i], ru[i], dg[i], du[i]);
-        (void)nb;
+        for (int i = 0; i < RING; i++) step(rx[i], rg[i], ru[i], dg[i], du[i]);
+    }
+    // split-K: waves 1..3 hand their partial sums to wave 0, which adds them in wave order
+    if (wave > 0) {
+        s_part[wave - 1][0][l] = ag;
+        s_part[wave - 1][1][l] = au;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < GU_SPLIT - 1; w++) {
+        ag += s_part[w][0][l];
+        au += s_part[w][1][l];
     }
     // D[m][c]: lane holds rows m = grp*4 + r, column c = l & 15 (feature f0 + c)
 #pragma unroll
@@ -215,8 +221,6 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ offsets, int H, int F, int E,
                                                     void* __restrict__ y) {
     __shared__ int s_info[3];
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float* asum = reinterpret_cast<float*>(smem);     // [16][F/32] (int4 only)
     const int tid = threadIdx.x;
     if (tid < WAVE) {
         int off = 0, n = 0;
@@ -226,75 +230,66 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
     __syncthreads();
     const int e = s_info[0], off = s_info[1], n = s_info[2];
     if (e < 0) return;
-    const int nb = F / 32;
-    if constexpr (WT == SDT_INT4) {
-        for (int i = tid; i < n * nb; i += blockDim.x) {
-            const int r = i / nb, b = i % nb;
-            const uint16_t* a = abuf + (long)(off + r) * F + b * 32;
-            float s = 0.f;
-            for (int k = 0; k < 32; k++) s += bf16_to_f32(a[k]);
-            asum[r * nb + b] = s;
-        }
-        __syncthreads();
-    }
     const int wave = tid / WAVE, l = lane_id();
     const int h0 = (blockIdx.y * 4 + wave) * 16;
-    if (h0 >= H) return;
     const int row = l & 15, grp = l >> 4;
     const bool arow = row < n;
     const uint16_t* ap = abuf + (long)(off + (arow ? row : 0)) * F + grp * 8;
+    const int steps = F / 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const int steps = nb;
     if constexpr (WT == SDT_BF16) {
         const uint16_t* pw = (const uint16_t*)wd_ + ((long)e * H + h0 + row) * F + grp * 8;
-        uint4 rw[RING];
+        uint4 rw[RING], ra[RING];
 #pragma unroll
-        for (int i = 0; i < RING; i++) rw[i] = *reinterpret_cast<const uint4*>(pw + i * 32);
+        for (int i = 0; i < RING; i++) {
+            rw[i] = ld_nt(pw + i * 32);
+            ra[i] = ld16(ap + i * 32);
+        }
         for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
             for (int i = 0; i < RING; i++) {
                 const int s = s0 + i;
-                const uint4 av = arow ? *reinterpret_cast<const uint4*>(ap + s * 32) : make_uint4(0, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rw[i]), acc, 0, 0, 0);
-                rw[i] = *reinterpret_cast<const uint4*>(pw + (s + RING) * 32);
+                acc = mfma(zero_unless(arow, ra[i]), rw[i], acc);
+                rw[i] = ld_nt(pw + (s + RING) * 32);
+                ra[i] = ld16(ap + (s + RING) * 32);
             }
         }
 #pragma unroll
-        for (int i = 0; i < RING; i++) {
-            const int s = steps - RING + i;
-            const uint4 av = arow ? *reinterpret_cast<const uint4*>(ap + s * 32) : make_uint4(0, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(rw[i]), acc, 0, 0, 0);
-        }
+        for (int i = 0; i < RING; i++) acc = mfma(zero_unless(arow, ra[i]), rw[i], acc);
     } else {
         const long rowg = (long)e * H + h0 + row;
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>((const uint8_t*)wd_ + rowg * (F / 2) + grp * 4);
-        const uint16_t* qd = sd + rowg * nb;
-        const float* as_r[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) as_r[r] = asum + (grp * 4 + r < n ? grp * 4 + r : 0) * nb;
+        const uint8_t* pw = (const uint8_t*)wd_ + rowg * (F / 2) + grp * 4;
+        const uint16_t* qd = sd + rowg * (F / 32);
         uint32_t rw[RING];
         uint16_t dw[RING];
+        uint4 ra[RING];
 #pragma unroll
-        for (int i = 0; i < RING; i++) { rw[i] = pw[i * 4]; dw[i] = qd[i]; }
-        auto step = [&](int s, uint32_t wq, uint16_t ds) __attribute__((always_inline)) {
-            const uint4 av = arow ? *reinterpret_cast<const uint4*>(ap + s * 32) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < RING; i++) {
+            rw[i] = ld_nt32(pw + i * 16);
+            dw[i] = qd[i];
+            ra[i] = ld16(ap + i * 32);
+        }
+        auto step = [&](uint4 a, uint32_t wq, uint16_t ds) __attribute__((always_inline)) {
+            const uint4 av = zero_unless(arow, a);
             const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(nib8_to_bf16_128(wq)), z, 0, 0, 0);
+            const f32x4_t S = mfma(av, bf16_ones(), z);
+            const f32x4_t D = mfma(av, nib8_to_bf16_128(wq), z);
             const float dc = fp16_to_f32(ds);
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[r] = fmaf(dc, D[r] - 136.0f * as_r[r][s], acc[r]);
+            for (int r = 0; r < 4; r++) acc[r] = fmaf(dc, fmaf(-136.0f, S[r], D[r]), acc[r]);
         };
         for (int s0 = 0; s0 < steps - RING; s0 += RING) {
 #pragma unroll
             for (int i = 0; i < RING; i++) {
                 const int s = s0 + i;
-                step(s, rw[i], dw[i]);
-                rw[i] = pw[(s + RING) * 4];
+                step(ra[i], rw[i], dw[i]);
+                rw[i] = ld_nt32(pw + (s + RING) * 16);
                 dw[i] = qd[s + RING];
+                ra[i] = ld16(ap + (s + RING) * 32);
             }
         }
 #pragma unroll
-        for (int i = 0; i < RING; i++) step(steps - RING + i, rw[i], dw[i]);
+        for (int i = 0; i < RING; i++) step(ra[i], rw[i], dw[i]);
     }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -314,22 +309,22 @@ static int ring_for(int steps) {
 }
 
 bool ffn_small_eligible(int T, int H, int F) {
-    return T <= SM_ROWS && H % 64 == 0 && F % 64 == 0;
+    return T <= SM_ROWS && H % (32 * GU_SPLIT) == 0 && F % 64 == 0 && H % 64 == 0;
 }
 
 template <int WT, int RG>
-static void gateup_small(dim3 g, size_t lds, hipStream_t st, const void* x, const void* wg, const void* wu,
-                         const void* sg, const void* su, const int32_t* offsets, const int32_t* perm, int K, int H,
-                         int F, int E, int rows_cap, uint16_t* abuf) {
-    hipLaunchKernelGGL((k_gateup_small<WT, RG>), g, dim3(256), lds, st, (const uint16_t*)x, wg, wu,
-                       (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, K, H, F, E, rows_cap, abuf);
+static void gateup_small(dim3 g, hipStream_t st, const void* x, const void* wg, const void* wu, const void* sg,
+                         const void* su, const int32_t* offsets, const int32_t* perm, int K, int H, int F, int E,
+                         uint16_t* abuf) {
+    hipLaunchKernelGGL((k_gateup_small<WT, RG>), g, dim3(256), 0, st, (const uint16_t*)x, wg, wu,
+                       (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, K, H, F, E, abuf);
 }
 
 template <int WT, int YB, int RG>
-static void down_small(dim3 g, size_t lds, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd,
+static void down_small(dim3 g, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd,
                        const int32_t* offsets, int H, int F, int E, void* y) {
-    hipLaunchKernelGGL((k_down_small<WT, YB, RG>), g, dim3(256), lds, st, abuf, wd, (const uint16_t*)sd, offsets, H,
-                       F, E, y);
+    hipLaunchKernelGGL((k_down_small<WT, YB, RG>), g, dim3(256), 0, st, abuf, wd, (const uint16_t*)sd, offsets, H, F,
+                       E, y);
 }
 
 template <int WT>
@@ -338,24 +333,22 @@ static void launch_wt(const void* x, const void* wg, const void* wu, const void*
                       void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
     const int n = T * K;
     const int slots = E < n ? E : n;          // at most this many experts are touched
-    const int rows_cap = T < SM_ROWS ? T : SM_ROWS;   // an expert has at most T rows
-    const size_t lds_g = (size_t)rows_cap * (H + 8) * 2 + (WT == SDT_INT4 ? (size_t)rows_cap * (H / 32) * 4 : 0);
-    const size_t lds_d = WT == SDT_INT4 ? (size_t)SM_ROWS * (F / 32) * 4 : 0;
-    dim3 gg(slots, F / 64), gd(slots, H / 64);
-    switch (ring_for(H / 32)) {
-        case 8: gateup_small<WT, 8>(gg, lds_g, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, rows_cap, abuf); break;
-        case 4: gateup_small<WT, 4>(gg, lds_g, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, rows_cap, abuf); break;
-        default: gateup_small<WT, 2>(gg, lds_g, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, rows_cap, abuf); break;
+    dim3 gg(slots, F / 16), gd(slots, H / 64);
+    switch (ring_for(H / 32 / GU_SPLIT)) {
+        case 8: gateup_small<WT, 8>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
+        case 4: gateup_small<WT, 4>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
+        case 2: gateup_small<WT, 2>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
+        default: gateup_small<WT, 1>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
     }
     const int rd = ring_for(F / 32);
     if (y_bf16) {
-        if (rd == 8) down_small<WT, 1, 8>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
-        else if (rd == 4) down_small<WT, 1, 4>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
-        else down_small<WT, 1, 2>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+        if (rd == 8) down_small<WT, 1, 8>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
+        else if (rd == 4) down_small<WT, 1, 4>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
+        else down_small<WT, 1, 2>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
     } else {
-        if (rd == 8) down_small<WT, 0, 8>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
-        else if (rd == 4) down_small<WT, 0, 4>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
-        else down_small<WT, 0, 2>(gd, lds_d, st, abuf, wd, sd, offsets, H, F, E, y);
+        if (rd == 8) down_small<WT, 0, 8>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
+        else if (rd == 4) down_small<WT, 0, 4>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
+        else down_small<WT, 0, 2>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
     }
 }
 

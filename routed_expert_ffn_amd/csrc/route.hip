@@ -303,7 +303,6 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
 // registers (H/64 independent loads per lane in flight); token rows are staged
 // in LDS.  Two experts per block.
 constexpr int XS_MAX_T = 16;
-constexpr int XS_MAX_HL = 64;     // H / 64 values per lane (H <= 4096)
 
 template <typename XT, int HL>
 __global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict__ x, const float* __restrict__ wr,
