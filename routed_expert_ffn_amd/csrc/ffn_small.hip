@@ -45,24 +45,34 @@ MOE_DEV uint4 zero_unless(bool keep, uint4 v) {
 }
 
 // The j-th expert with a non-empty segment (-1 if none); result in every lane.
+// The offsets of up to 512 experts are fetched in one batch of independent
+// loads (one memory round trip), then scanned.
 MOE_DEV int find_touched(const int32_t* __restrict__ offsets, int E, int j, int& off, int& n) {
     const int l = lane_id();
     int base = 0;
-    for (int e0 = 0; e0 < E; e0 += WAVE) {
-        const int e = e0 + l;
-        int o = 0, c = 0;
-        if (e < E) { o = offsets[e]; c = offsets[e + 1] - o; }
-        const int t = c > 0 ? 1 : 0;
-        const int incl = wave_incl_scan(t);
-        const bool hit = t && (base + incl - 1 == j);
-        const unsigned long long m = __ballot(hit);
-        if (m) {
-            const int src = __ffsll((long long)m) - 1;
-            off = __shfl(o, src, WAVE);
-            n = __shfl(c, src, WAVE);
-            return e0 + src;
+    for (int p0 = 0; p0 < E; p0 += 8 * WAVE) {
+        int o[8], c[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int e = p0 + q * WAVE + l;
+            const int ec = e < E ? e : E;
+            o[q] = offsets[ec];
+            c[q] = offsets[ec + (e < E ? 1 : 0)];
         }
-        base += __shfl(incl, WAVE - 1, WAVE);
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            c[q] -= o[q];
+            const int t = c[q] > 0 ? 1 : 0;
+            const int incl = wave_incl_scan(t);
+            const unsigned long long m = __ballot(t && (base + incl - 1 == j));
+            if (m) {
+                const int src = __ffsll((long long)m) - 1;
+                off = __shfl(o[q], src, WAVE);
+                n = __shfl(c[q], src, WAVE);
+                return p0 + q * WAVE + src;
+            }
+            base += __shfl(incl, WAVE - 1, WAVE);
+        }
     }
     return -1;
 }
