@@ -312,6 +312,174 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------- bf16: VALU dot products
+//
+// For bf16 weights the streaming pattern that HBM serves best is one
+// contiguous 1 KB chunk of a single weight row per wave instruction (64 lanes
+// x 16 B); the 16-row MFMA operand layout (16 rows x 64 B per instruction)
+// loses ~30% of the bandwidth at these sizes.  So here each lane multiplies its
+// 8 weights by the matching 8 activations of every token row with
+// v_dot2_f32_bf16, and the per-lane partial sums are combined across the wave
+// by a transposing butterfly: with V sums per lane, each xor step keeps half of
+// them and adds the partner's copy of that half, so after log2(V) steps lane l
+// holds the full sum of entry l >> (6 - log2 V) (remaining steps add copies).
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+MOE_DEV float dot8(uint4 w, uint4 x, float c) {
+    c = dot2(w.x, x.x, c);
+    c = dot2(w.y, x.y, c);
+    c = dot2(w.z, x.z, c);
+    return dot2(w.w, x.w, c);
+}
+
+// One butterfly step of the transposing reduction (CNT live entries, xor
+// distance D); fully unrolled at compile time so v[] stays in registers.
+template <int CNT, int D, int V>
+MOE_DEV void transpose_reduce_step(float (&v)[V], int l) {
+    if constexpr (D >= 1) {
+        if constexpr (CNT > 1) {
+            constexpr int half = CNT / 2;
+            const bool bit = (l & D) != 0;
+#pragma unroll
+            for (int i = 0; i < half; i++) {
+                const float keep = bit ? v[i + half] : v[i];
+                const float send = bit ? v[i] : v[i + half];
+                v[i] = keep + __shfl_xor(send, D, WAVE);
+            }
+            transpose_reduce_step<half, D / 2, V>(v, l);
+        } else {
+            v[0] += __shfl_xor(v[0], D, WAVE);
+            transpose_reduce_step<1, D / 2, V>(v, l);
+        }
+    }
+}
+
+// In-place transposing reduction of v[V] over the wave; returns the sum of
+// entry lane >> (6 - log2 V).
+template <int V>
+MOE_DEV float wave_transpose_reduce(float (&v)[V]) {
+    transpose_reduce_step<V, 32, V>(v, lane_id());
+    return v[0];
+}
+
+constexpr int GV_WAVES = 8;    // gate/up block: 8 waves x 2 feature rows (gate and up each)
+constexpr int DV_ROWS = 8;     // down: hidden rows per wave
+
+template <int NT, int CH>
+__global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
+                                                     const uint16_t* __restrict__ wu,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ perm, int K, int H, int F, int E,
+                                                     uint16_t* __restrict__ abuf) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);          // [n][H]
+    __shared__ int s_info[3];
+    const int tid = threadIdx.x;
+    if (tid < WAVE) {
+        int off = 0, n = 0;
+        const int e = find_touched(offsets, E, blockIdx.x, off, n);
+        if (tid == 0) { s_info[0] = e; s_info[1] = off; s_info[2] = n; }
+    }
+    __syncthreads();
+    const int e = s_info[0], off = s_info[1], n = s_info[2];
+    if (e < 0) return;
+    const int wave = tid / WAVE, l = lane_id();
+    const int f0 = blockIdx.y * (2 * GV_WAVES) + wave * 2;
+    constexpr int chunks = CH;                  // 1 KB chunks per row: H = 512 * CH
+    // this wave's 4 weight rows: gate f0, f0+1, up f0, f0+1; issue every chunk load now
+    const uint16_t* g0 = wg + ((long)e * F + f0) * H + l * 8;
+    const uint16_t* u0 = wu + ((long)e * F + f0) * H + l * 8;
+    uint4 w[4][CH];
+#pragma unroll
+    for (int c = 0; c < chunks; c++) {
+        w[0][c] = ld_nt(g0 + c * 512);
+        w[1][c] = ld_nt(g0 + H + c * 512);
+        w[2][c] = ld_nt(u0 + c * 512);
+        w[3][c] = ld_nt(u0 + H + c * 512);
+    }
+    // stage the expert's token rows in LDS while the weights are in flight
+    const int row_chunks = H / 8;
+    for (int i = tid; i < n * row_chunks; i += blockDim.x) {
+        const int r = i / row_chunks, c8 = (i % row_chunks) * 8;
+        const long t = perm[off + r] / K;
+        *reinterpret_cast<uint4*>(&xs[r * H + c8]) = ld16(x + t * H + c8);
+    }
+    __syncthreads();
+    float acc[4 * NT];
+#pragma unroll
+    for (int i = 0; i < 4 * NT; i++) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < chunks; c++) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(&xs[(t < n ? t : 0) * H + c * 512 + l * 8]);
+            const uint4 a = zero_unless(t < n, xv);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
+        }
+    }
+    // lane l now owns entry j = l >> shift: row r = j / NT (0,1 gate; 2,3 up), token t = j % NT
+    const float v = wave_transpose_reduce<4 * NT>(acc);
+    constexpr int V = 4 * NT;
+    constexpr int shift = V == 16 ? 2 : V == 32 ? 1 : 0;
+    const float up = __shfl_down(v, (2 * NT) << shift, WAVE);   // entry j + 2*NT: the matching up row
+    const int j = l >> shift;
+    const int r = j / NT, t = j % NT;
+    if ((l & ((1 << shift) - 1)) == 0 && r < 2 && t < n)
+        abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_s(v) * up);
+}
+
+template <int NT, int YBF16, int FCH>
+__global__ __launch_bounds__(256) void k_down_valu(const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ wd,
+                                                   const int32_t* __restrict__ offsets, int H, int F, int E,
+                                                   void* __restrict__ y) {
+    __shared__ int s_info[3];
+    const int tid = threadIdx.x;
+    if (tid < WAVE) {
+        int off = 0, n = 0;
+        const int e = find_touched(offsets, E, blockIdx.x, off, n);
+        if (tid == 0) { s_info[0] = e; s_info[1] = off; s_info[2] = n; }
+    }
+    __syncthreads();
+    const int e = s_info[0], off = s_info[1], n = s_info[2];
+    if (e < 0) return;
+    const int wave = tid / WAVE, l = lane_id();
+    const int h0 = (blockIdx.y * 4 + wave) * DV_ROWS;
+    constexpr int chunks = FCH;                 // 1 KB chunks per row: F = 512 * FCH
+    uint4 w[DV_ROWS][FCH];
+#pragma unroll
+    for (int c = 0; c < chunks; c++) {
+#pragma unroll
+        for (int r = 0; r < DV_ROWS; r++) w[r][c] = ld_nt(wd + ((long)e * H + h0 + r) * F + c * 512 + l * 8);
+    }
+    float acc[DV_ROWS * NT];
+#pragma unroll
+    for (int i = 0; i < DV_ROWS * NT; i++) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < chunks; c++) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const uint4 av = ld16(abuf + (long)(off + (t < n ? t : 0)) * F + c * 512 + l * 8);
+            const uint4 a = zero_unless(t < n, av);
+#pragma unroll
+            for (int r = 0; r < DV_ROWS; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
+        }
+    }
+    constexpr int V = DV_ROWS * NT;
+    const float v = wave_transpose_reduce<V>(acc);
+    constexpr int shift = V == 32 ? 1 : 0;      // V = 32 or 64 (NT = 4 or 8)
+    const int j = l >> shift;
+    const int r = j / NT, t = j % NT;
+    if ((l & ((1 << shift) - 1)) == 0 && t < n) {
+        const long o = (long)(off + t) * H + h0 + r;
+        if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
+        else ((float*)y)[o] = v;
+    }
+}
+
 // ---------------------------------------------------------------------------- host
 
 static int ring_for(int steps) {
@@ -362,11 +530,57 @@ static void launch_wt(const void* x, const void* wg, const void* wu, const void*
     }
 }
 
+template <int NT, int CH, int FCH>
+static void launch_valu(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                        const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, uint16_t* abuf,
+                        hipStream_t st) {
+    const int n = T * K;
+    const int slots = E < n ? E : n;
+    const int rows_cap = T < NT ? T : NT;
+    dim3 gg(slots, F / (2 * GV_WAVES)), gd(slots, H / (4 * DV_ROWS));
+    hipLaunchKernelGGL((k_gateup_valu<NT, CH>), gg, dim3(64 * GV_WAVES), (size_t)rows_cap * H * 2, st,
+                       (const uint16_t*)x, (const uint16_t*)wg, (const uint16_t*)wu, offsets, perm, K, H, F, E, abuf);
+    if (y_bf16)
+        hipLaunchKernelGGL((k_down_valu<NT, 1, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, offsets, H, F,
+                           E, y);
+    else
+        hipLaunchKernelGGL((k_down_valu<NT, 0, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, offsets, H, F,
+                           E, y);
+}
+
+template <int NT, int CH>
+static void launch_valu_f(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                          const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16,
+                          uint16_t* abuf, hipStream_t st) {
+    if (F == 512) launch_valu<NT, CH, 1>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+    else launch_valu<NT, CH, 2>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+}
+
+template <int NT>
+static void launch_valu_h(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                          const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16,
+                          uint16_t* abuf, hipStream_t st) {
+    switch (H / 512) {
+        case 1: launch_valu_f<NT, 1>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
+        case 2: launch_valu_f<NT, 2>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
+        case 4: launch_valu_f<NT, 4>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
+        default: launch_valu_f<NT, 8>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
+    }
+}
+
 hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const void* wu, const void* wd,
                             const void* sg, const void* su, const void* sd, const int32_t* offsets,
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                             hipStream_t st) {
     uint16_t* abuf = (uint16_t*)ws;
+    // bf16, T <= 8, H and F whole 1 KB chunks: contiguous-row VALU kernels
+    const int hc = H / 512;
+    if (w_dtype == SDT_BF16 && T <= 8 && H % 512 == 0 && (hc == 1 || hc == 2 || hc == 4 || hc == 8) &&
+        (F == 512 || F == 1024)) {
+        if (T <= 4) launch_valu_h<4>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+        else launch_valu_h<8>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+        return hipGetLastError();
+    }
     if (w_dtype == SDT_BF16)
         launch_wt<SDT_BF16>(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
     else
