@@ -335,10 +335,15 @@ __global__ __launch_bounds__(256) void k_down_f32(const float* __restrict__ abuf
 // ---- host ------------------------------------------------------------------------
 
 size_t ffn_workspace_bytes(int T, int K, int E, int H, int F, int x_dtype, int w_dtype) {
-    (void)E; (void)H; (void)w_dtype;
+    (void)w_dtype;
     const size_t n = (size_t)T * K;
     const size_t elt = x_dtype == DT_F32 ? 4 : 2;
-    return ((n * F * elt) + 255) / 256 * 256;
+    size_t b = ((n * F * elt) + 255) / 256 * 256;
+    if (x_dtype != DT_F32 && ffn_small_eligible(T, H, F)) {
+        const size_t s = ffn_small_workspace_bytes(T, K, E, H, F);
+        b = s > b ? s : b;
+    }
+    return b;
 }
 
 hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, const void* wu, const void* wd,

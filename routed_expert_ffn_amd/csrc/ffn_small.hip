@@ -15,8 +15,11 @@
 //     H, partial sums added through LDS in a fixed order), so a block is 16
 //     feature rows of gate AND up and the grid has enough blocks to fill all
 //     CUs; down gives each wave 16 hidden rows over the full (short) K = F.
-//   * a block finds its expert by a wave-wide scan of the expert offsets, so
-//     the grid only depends on T*K.
+//   * a small preparation kernel lists the touched experts and gathers the
+//     token rows in grouped order, so every FFN block starts streaming after
+//     one dependent load; the grid only depends on T*K, and blockIdx.x runs
+//     over the tiles of one expert (blocks dispatched together read one
+//     expert's matrix contiguously).
 // int4 weights: each 32-element block along K is one MFMA K step.  The
 // nibbles u become the bf16 values 128 + u (bit pattern 0x4300 | u, exact);
 // with the weight d (u - 8):
@@ -44,37 +47,35 @@ MOE_DEV uint4 zero_unless(bool keep, uint4 v) {
     return keep ? v : make_uint4(0, 0, 0, 0);
 }
 
-// The j-th expert with a non-empty segment (-1 if none); result in every lane.
-// The offsets of up to 512 experts are fetched in one batch of independent
-// loads (one memory round trip), then scanned.
-MOE_DEV int find_touched(const int32_t* __restrict__ offsets, int E, int j, int& off, int& n) {
+// Preparation (one small kernel ahead of the FFN kernels, so their blocks
+// start streaming weights after a single dependent load):
+//   * list[j] = (expert, first row, rows) of the j-th expert with rows, in
+//     expert order; entries past the last touched expert hold expert -1;
+//   * xp[p] = x[perm[p] / K]: the token rows gathered in grouped order.
+__global__ __launch_bounds__(256) void k_small_prep(const uint16_t* __restrict__ x,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ perm, int K, int H, int E, int n,
+                                                    int slots, int4* __restrict__ list, uint16_t* __restrict__ xp) {
+    const int row_chunks = H / 8;
+    const long total = (long)n * row_chunks;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+        const int r = (int)(i / row_chunks), c = (int)(i % row_chunks) * 8;
+        const long t = perm[r] / K;
+        *reinterpret_cast<uint4*>(xp + (long)r * H + c) = *reinterpret_cast<const uint4*>(x + t * H + c);
+    }
+    if (blockIdx.x != 0 || threadIdx.x >= WAVE) return;
     const int l = lane_id();
     int base = 0;
-    for (int p0 = 0; p0 < E; p0 += 8 * WAVE) {
-        int o[8], c[8];
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const int e = p0 + q * WAVE + l;
-            const int ec = e < E ? e : E;
-            o[q] = offsets[ec];
-            c[q] = offsets[ec + (e < E ? 1 : 0)];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-            c[q] -= o[q];
-            const int t = c[q] > 0 ? 1 : 0;
-            const int incl = wave_incl_scan(t);
-            const unsigned long long m = __ballot(t && (base + incl - 1 == j));
-            if (m) {
-                const int src = __ffsll((long long)m) - 1;
-                off = __shfl(o[q], src, WAVE);
-                n = __shfl(c[q], src, WAVE);
-                return p0 + q * WAVE + src;
-            }
-            base += __shfl(incl, WAVE - 1, WAVE);
-        }
+    for (int e0 = 0; e0 < E; e0 += WAVE) {
+        const int e = e0 + l;
+        int o = 0, c = 0;
+        if (e < E) { o = offsets[e]; c = offsets[e + 1] - o; }
+        const int t = c > 0 ? 1 : 0;
+        const int incl = wave_incl_scan(t);
+        if (t) list[base + incl - 1] = make_int4(e, o, c, 0);
+        base += __shfl(incl, WAVE - 1, WAVE);
     }
-    return -1;
+    for (int j = base + l; j < slots; j += WAVE) list[j] = make_int4(-1, 0, 0, 0);
 }
 
 MOE_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -101,31 +102,22 @@ MOE_DEV f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 // ---------------------------------------------------------------------------- gate/up
 
 template <int WT, int RING>
-__global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict__ x, const void* __restrict__ wg_,
+__global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict__ xp, const void* __restrict__ wg_,
                                                       const void* __restrict__ wu_, const uint16_t* __restrict__ sg,
-                                                      const uint16_t* __restrict__ su,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ perm, int K, int H, int F, int E,
-                                                      uint16_t* __restrict__ abuf) {
-    __shared__ int s_info[3];
+                                                      const uint16_t* __restrict__ su, const int4* __restrict__ list,
+                                                      int H, int F, uint16_t* __restrict__ abuf) {
     __shared__ f32x4_t s_part[GU_SPLIT - 1][2][WAVE];
     const int tid = threadIdx.x;
-    if (tid < WAVE) {
-        int off = 0, n = 0;
-        const int e = find_touched(offsets, E, blockIdx.x, off, n);
-        if (tid == 0) { s_info[0] = e; s_info[1] = off; s_info[2] = n; }
-    }
-    __syncthreads();
-    const int e = s_info[0], off = s_info[1], n = s_info[2];
+    const int4 ent = list[blockIdx.y];
+    const int e = ent.x, off = ent.y, n = ent.z;
     if (e < 0) return;
     const int wave = tid / WAVE, l = lane_id();
-    const int f0 = blockIdx.y * 16;
+    const int f0 = blockIdx.x * 16;
     const int row = l & 15, grp = l >> 4;
     const bool arow = row < n;
-    const long tok = perm[off + (arow ? row : 0)] / K;
     const int steps = H / 32 / GU_SPLIT;            // K steps of this wave
     const int k0 = wave * steps * 32;               // this wave's quarter of H
-    const uint16_t* xa = x + tok * H + k0 + grp * 8;
+    const uint16_t* xa = xp + (long)(off + (arow ? row : 0)) * H + k0 + grp * 8;
 
     f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
     if constexpr (WT == SDT_BF16) {
@@ -227,21 +219,14 @@ __global__ __launch_bounds__(256) void k_gateup_small(const uint16_t* __restrict
 
 template <int WT, int YBF16, int RING>
 __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__ abuf, const void* __restrict__ wd_,
-                                                    const uint16_t* __restrict__ sd,
-                                                    const int32_t* __restrict__ offsets, int H, int F, int E,
-                                                    void* __restrict__ y) {
-    __shared__ int s_info[3];
+                                                    const uint16_t* __restrict__ sd, const int4* __restrict__ list,
+                                                    int H, int F, void* __restrict__ y) {
     const int tid = threadIdx.x;
-    if (tid < WAVE) {
-        int off = 0, n = 0;
-        const int e = find_touched(offsets, E, blockIdx.x, off, n);
-        if (tid == 0) { s_info[0] = e; s_info[1] = off; s_info[2] = n; }
-    }
-    __syncthreads();
-    const int e = s_info[0], off = s_info[1], n = s_info[2];
+    const int4 ent = list[blockIdx.y];
+    const int e = ent.x, off = ent.y, n = ent.z;
     if (e < 0) return;
     const int wave = tid / WAVE, l = lane_id();
-    const int h0 = (blockIdx.y * 4 + wave) * 16;
+    const int h0 = (blockIdx.x * 4 + wave) * 16;
     const int row = l & 15, grp = l >> 4;
     const bool arow = row < n;
     const uint16_t* ap = abuf + (long)(off + (arow ? row : 0)) * F + grp * 8;
@@ -369,27 +354,16 @@ constexpr int GV_WAVES = 8;    // gate/up block: 8 waves x 2 feature rows (gate 
 constexpr int DV_ROWS = 8;     // down: hidden rows per wave
 
 template <int NT, int CH>
-__global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
-                                                     const uint16_t* __restrict__ wu,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ perm, int K, int H, int F, int E,
-                                                     uint16_t* __restrict__ abuf) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);          // [n][H]
-    __shared__ int s_info[3];
-    const int tid = threadIdx.x;
-    if (tid < WAVE) {
-        int off = 0, n = 0;
-        const int e = find_touched(offsets, E, blockIdx.x, off, n);
-        if (tid == 0) { s_info[0] = e; s_info[1] = off; s_info[2] = n; }
-    }
-    __syncthreads();
-    const int e = s_info[0], off = s_info[1], n = s_info[2];
+__global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict__ xp, const uint16_t* __restrict__ wg,
+                                                     const uint16_t* __restrict__ wu, const int4* __restrict__ list,
+                                                     int H, int F, uint16_t* __restrict__ abuf) {
+    const int4 ent = list[blockIdx.y];
+    const int e = ent.x, off = ent.y, n = ent.z;
     if (e < 0) return;
-    const int wave = tid / WAVE, l = lane_id();
-    const int f0 = blockIdx.y * (2 * GV_WAVES) + wave * 2;
+    const int wave = threadIdx.x / WAVE, l = lane_id();
+    const int f0 = blockIdx.x * (2 * GV_WAVES) + wave * 2;
     constexpr int chunks = CH;                  // 1 KB chunks per row: H = 512 * CH
-    // this wave's 4 weight rows: gate f0, f0+1, up f0, f0+1; issue every chunk load now
+    // this wave's 4 weight rows (gate f0, f0+1, up f0, f0+1) and the token rows' matching chunks
     const uint16_t* g0 = wg + ((long)e * F + f0) * H + l * 8;
     const uint16_t* u0 = wu + ((long)e * F + f0) * H + l * 8;
     uint4 w[4][CH];
@@ -400,14 +374,6 @@ __global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict_
         w[2][c] = ld_nt(u0 + c * 512);
         w[3][c] = ld_nt(u0 + H + c * 512);
     }
-    // stage the expert's token rows in LDS while the weights are in flight
-    const int row_chunks = H / 8;
-    for (int i = tid; i < n * row_chunks; i += blockDim.x) {
-        const int r = i / row_chunks, c8 = (i % row_chunks) * 8;
-        const long t = perm[off + r] / K;
-        *reinterpret_cast<uint4*>(&xs[r * H + c8]) = ld16(x + t * H + c8);
-    }
-    __syncthreads();
     float acc[4 * NT];
 #pragma unroll
     for (int i = 0; i < 4 * NT; i++) acc[i] = 0.f;
@@ -415,7 +381,7 @@ __global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict_
     for (int c = 0; c < chunks; c++) {
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(&xs[(t < n ? t : 0) * H + c * 512 + l * 8]);
+            const uint4 xv = ld16(xp + (long)(off + (t < n ? t : 0)) * H + c * 512 + l * 8);
             const uint4 a = zero_unless(t < n, xv);
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
@@ -434,20 +400,13 @@ __global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict_
 
 template <int NT, int YBF16, int FCH>
 __global__ __launch_bounds__(256) void k_down_valu(const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ wd,
-                                                   const int32_t* __restrict__ offsets, int H, int F, int E,
+                                                   const int4* __restrict__ list, int H, int F,
                                                    void* __restrict__ y) {
-    __shared__ int s_info[3];
-    const int tid = threadIdx.x;
-    if (tid < WAVE) {
-        int off = 0, n = 0;
-        const int e = find_touched(offsets, E, blockIdx.x, off, n);
-        if (tid == 0) { s_info[0] = e; s_info[1] = off; s_info[2] = n; }
-    }
-    __syncthreads();
-    const int e = s_info[0], off = s_info[1], n = s_info[2];
+    const int4 ent = list[blockIdx.y];
+    const int e = ent.x, off = ent.y, n = ent.z;
     if (e < 0) return;
-    const int wave = tid / WAVE, l = lane_id();
-    const int h0 = (blockIdx.y * 4 + wave) * DV_ROWS;
+    const int wave = threadIdx.x / WAVE, l = lane_id();
+    const int h0 = (blockIdx.x * 4 + wave) * DV_ROWS;
     constexpr int chunks = FCH;                 // 1 KB chunks per row: F = 512 * FCH
     uint4 w[DV_ROWS][FCH];
 #pragma unroll
@@ -490,81 +449,77 @@ bool ffn_small_eligible(int T, int H, int F) {
     return T <= SM_ROWS && H % (32 * GU_SPLIT) == 0 && F % 64 == 0 && H % 64 == 0;
 }
 
+static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace of the small path: [A: n x F bf16][list: slots x int4][xp: n x H bf16].
+size_t ffn_small_workspace_bytes(int T, int K, int E, int H, int F) {
+    const size_t n = (size_t)T * K, slots = (size_t)(E < (int)n ? E : (int)n);
+    return al256(n * F * 2) + al256(slots * 16) + al256(n * H * 2);
+}
+
 template <int WT, int RG>
-static void gateup_small(dim3 g, hipStream_t st, const void* x, const void* wg, const void* wu, const void* sg,
-                         const void* su, const int32_t* offsets, const int32_t* perm, int K, int H, int F, int E,
-                         uint16_t* abuf) {
-    hipLaunchKernelGGL((k_gateup_small<WT, RG>), g, dim3(256), 0, st, (const uint16_t*)x, wg, wu,
-                       (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, K, H, F, E, abuf);
+static void gateup_small(dim3 g, hipStream_t st, const uint16_t* xp, const void* wg, const void* wu, const void* sg,
+                         const void* su, const int4* list, int H, int F, uint16_t* abuf) {
+    hipLaunchKernelGGL((k_gateup_small<WT, RG>), g, dim3(256), 0, st, xp, wg, wu, (const uint16_t*)sg,
+                       (const uint16_t*)su, list, H, F, abuf);
 }
 
 template <int WT, int YB, int RG>
-static void down_small(dim3 g, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd,
-                       const int32_t* offsets, int H, int F, int E, void* y) {
-    hipLaunchKernelGGL((k_down_small<WT, YB, RG>), g, dim3(256), 0, st, abuf, wd, (const uint16_t*)sd, offsets, H, F,
-                       E, y);
+static void down_small(dim3 g, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd, const int4* list,
+                       int H, int F, void* y) {
+    hipLaunchKernelGGL((k_down_small<WT, YB, RG>), g, dim3(256), 0, st, abuf, wd, (const uint16_t*)sd, list, H, F, y);
 }
 
 template <int WT>
-static void launch_wt(const void* x, const void* wg, const void* wu, const void* wd, const void* sg, const void* su,
-                      const void* sd, const int32_t* offsets, const int32_t* perm, int T, int K, int H, int F, int E,
-                      void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
-    const int n = T * K;
-    const int slots = E < n ? E : n;          // at most this many experts are touched
-    dim3 gg(slots, F / 16), gd(slots, H / 64);
+static void launch_wt(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const void* sg,
+                      const void* su, const void* sd, const int4* list, int slots, int H, int F, void* y,
+                      int y_bf16, uint16_t* abuf, hipStream_t st) {
+    dim3 gg(F / 16, slots), gd(H / 64, slots);
     switch (ring_for(H / 32 / GU_SPLIT)) {
-        case 8: gateup_small<WT, 8>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
-        case 4: gateup_small<WT, 4>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
-        case 2: gateup_small<WT, 2>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
-        default: gateup_small<WT, 1>(gg, st, x, wg, wu, sg, su, offsets, perm, K, H, F, E, abuf); break;
+        case 8: gateup_small<WT, 8>(gg, st, xp, wg, wu, sg, su, list, H, F, abuf); break;
+        case 4: gateup_small<WT, 4>(gg, st, xp, wg, wu, sg, su, list, H, F, abuf); break;
+        case 2: gateup_small<WT, 2>(gg, st, xp, wg, wu, sg, su, list, H, F, abuf); break;
+        default: gateup_small<WT, 1>(gg, st, xp, wg, wu, sg, su, list, H, F, abuf); break;
     }
     const int rd = ring_for(F / 32);
     if (y_bf16) {
-        if (rd == 8) down_small<WT, 1, 8>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
-        else if (rd == 4) down_small<WT, 1, 4>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
-        else down_small<WT, 1, 2>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
+        if (rd == 8) down_small<WT, 1, 8>(gd, st, abuf, wd, sd, list, H, F, y);
+        else if (rd == 4) down_small<WT, 1, 4>(gd, st, abuf, wd, sd, list, H, F, y);
+        else down_small<WT, 1, 2>(gd, st, abuf, wd, sd, list, H, F, y);
     } else {
-        if (rd == 8) down_small<WT, 0, 8>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
-        else if (rd == 4) down_small<WT, 0, 4>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
-        else down_small<WT, 0, 2>(gd, st, abuf, wd, sd, offsets, H, F, E, y);
+        if (rd == 8) down_small<WT, 0, 8>(gd, st, abuf, wd, sd, list, H, F, y);
+        else if (rd == 4) down_small<WT, 0, 4>(gd, st, abuf, wd, sd, list, H, F, y);
+        else down_small<WT, 0, 2>(gd, st, abuf, wd, sd, list, H, F, y);
     }
 }
 
 template <int NT, int CH, int FCH>
-static void launch_valu(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
-                        const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, uint16_t* abuf,
-                        hipStream_t st) {
-    const int n = T * K;
-    const int slots = E < n ? E : n;
-    const int rows_cap = T < NT ? T : NT;
-    dim3 gg(slots, F / (2 * GV_WAVES)), gd(slots, H / (4 * DV_ROWS));
-    hipLaunchKernelGGL((k_gateup_valu<NT, CH>), gg, dim3(64 * GV_WAVES), (size_t)rows_cap * H * 2, st,
-                       (const uint16_t*)x, (const uint16_t*)wg, (const uint16_t*)wu, offsets, perm, K, H, F, E, abuf);
+static void launch_valu(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
+                        int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
+    dim3 gg(F / (2 * GV_WAVES), slots), gd(H / (4 * DV_ROWS), slots);
+    hipLaunchKernelGGL((k_gateup_valu<NT, CH>), gg, dim3(64 * GV_WAVES), 0, st, xp, (const uint16_t*)wg,
+                       (const uint16_t*)wu, list, H, F, abuf);
     if (y_bf16)
-        hipLaunchKernelGGL((k_down_valu<NT, 1, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, offsets, H, F,
-                           E, y);
+        hipLaunchKernelGGL((k_down_valu<NT, 1, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, list, H, F, y);
     else
-        hipLaunchKernelGGL((k_down_valu<NT, 0, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, offsets, H, F,
-                           E, y);
+        hipLaunchKernelGGL((k_down_valu<NT, 0, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, list, H, F, y);
 }
 
 template <int NT, int CH>
-static void launch_valu_f(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
-                          const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16,
-                          uint16_t* abuf, hipStream_t st) {
-    if (F == 512) launch_valu<NT, CH, 1>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
-    else launch_valu<NT, CH, 2>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+static void launch_valu_f(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
+                          int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
+    if (F == 512) launch_valu<NT, CH, 1>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
+    else launch_valu<NT, CH, 2>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
 }
 
 template <int NT>
-static void launch_valu_h(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
-                          const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16,
-                          uint16_t* abuf, hipStream_t st) {
+static void launch_valu_h(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
+                          int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
     switch (H / 512) {
-        case 1: launch_valu_f<NT, 1>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
-        case 2: launch_valu_f<NT, 2>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
-        case 4: launch_valu_f<NT, 4>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
-        default: launch_valu_f<NT, 8>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st); break;
+        case 1: launch_valu_f<NT, 1>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
+        case 2: launch_valu_f<NT, 2>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
+        case 4: launch_valu_f<NT, 4>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
+        default: launch_valu_f<NT, 8>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
     }
 }
 
@@ -572,18 +527,27 @@ hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const vo
                             const void* sg, const void* su, const void* sd, const int32_t* offsets,
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                             hipStream_t st) {
-    uint16_t* abuf = (uint16_t*)ws;
-    // bf16, T <= 8, H and F whole 1 KB chunks: contiguous-row VALU kernels
+    const int n = T * K;
+    const int slots = E < n ? E : n;          // at most this many experts are touched
+    char* base = (char*)ws;
+    uint16_t* abuf = (uint16_t*)base;
+    int4* list = (int4*)(base + al256((size_t)n * F * 2));
+    uint16_t* xp = (uint16_t*)(base + al256((size_t)n * F * 2) + al256((size_t)slots * 16));
+    const long chunks = (long)n * H / 8;
+    const int prep_blocks = (int)((chunks + 255) / 256);
+    hipLaunchKernelGGL(k_small_prep, dim3(prep_blocks > 0 ? prep_blocks : 1), dim3(256), 0, st, (const uint16_t*)x,
+                       offsets, perm, K, H, E, n, slots, list, xp);
+    // bf16, T <= 8, whole 1 KB rows: contiguous-row VALU kernels
     const int hc = H / 512;
     if (w_dtype == SDT_BF16 && T <= 8 && H % 512 == 0 && (hc == 1 || hc == 2 || hc == 4 || hc == 8) &&
         (F == 512 || F == 1024)) {
-        if (T <= 4) launch_valu_h<4>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
-        else launch_valu_h<8>(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+        if (T <= 4) launch_valu_h<4>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
+        else launch_valu_h<8>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
         return hipGetLastError();
     }
     if (w_dtype == SDT_BF16)
-        launch_wt<SDT_BF16>(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+        launch_wt<SDT_BF16>(xp, wg, wu, wd, sg, su, sd, list, slots, H, F, y, y_bf16, abuf, st);
     else
-        launch_wt<SDT_INT4>(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, abuf, st);
+        launch_wt<SDT_INT4>(xp, wg, wu, wd, sg, su, sd, list, slots, H, F, y, y_bf16, abuf, st);
     return hipGetLastError();
 }

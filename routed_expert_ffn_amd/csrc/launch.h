@@ -26,6 +26,7 @@ hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, c
 
 // ffn_small.hip (every expert has <= 16 rows)
 bool ffn_small_eligible(int T, int H, int F);
+size_t ffn_small_workspace_bytes(int T, int K, int E, int H, int F);
 hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const void* wu, const void* wd,
                             const void* sg, const void* su, const void* sd, const int32_t* offsets,
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
