@@ -26,6 +26,9 @@
 //     sum_k x w = d (D - 136 S),  D = MFMA(x, 128 + u),  S = MFMA(x, 1)
 // so the row sums S come out of the same MFMA layout, and the weights enter
 // exactly (no rounding of d * q).
+#include <cstdio>
+#include <cstdlib>
+
 #include "common.h"
 #include "launch.h"
 
@@ -350,86 +353,99 @@ MOE_DEV float wave_transpose_reduce(float (&v)[V]) {
     return v[0];
 }
 
-constexpr int GV_WAVES = 8;    // gate/up block: 8 waves x 2 feature rows (gate and up each)
-constexpr int DV_ROWS = 8;     // down: hidden rows per wave
-
-template <int NT, int CH>
-__global__ __launch_bounds__(512) void k_gateup_valu(const uint16_t* __restrict__ xp, const uint16_t* __restrict__ wg,
-                                                     const uint16_t* __restrict__ wu, const int4* __restrict__ list,
-                                                     int H, int F, uint16_t* __restrict__ abuf) {
+// gate/up: a wave owns FR feature rows (FR gate rows and the same FR up rows)
+// over the whole of H; WV waves per block share the expert's token rows in LDS.
+template <int NT, int CH, int FR, int WV>
+__global__ __launch_bounds__(64 * WV) void k_gateup_valu(const uint16_t* __restrict__ xp,
+                                                         const uint16_t* __restrict__ wg,
+                                                         const uint16_t* __restrict__ wu,
+                                                         const int4* __restrict__ list, int H, int F,
+                                                         uint16_t* __restrict__ abuf) {
     const int4 ent = list[blockIdx.y];
     const int e = ent.x, off = ent.y, n = ent.z;
     if (e < 0) return;
     const int wave = threadIdx.x / WAVE, l = lane_id();
-    const int f0 = blockIdx.x * (2 * GV_WAVES) + wave * 2;
-    constexpr int chunks = CH;                  // 1 KB chunks per row: H = 512 * CH
-    // this wave's 4 weight rows (gate f0, f0+1, up f0, f0+1) and the token rows' matching chunks
+    const int f0 = (blockIdx.x * WV + wave) * FR;
+    // this wave's weight rows (gate f0.., up f0..), every 1 KB chunk in flight at once
     const uint16_t* g0 = wg + ((long)e * F + f0) * H + l * 8;
     const uint16_t* u0 = wu + ((long)e * F + f0) * H + l * 8;
-    uint4 w[4][CH];
+    uint4 w[2 * FR][CH];
 #pragma unroll
-    for (int c = 0; c < chunks; c++) {
-        w[0][c] = ld_nt(g0 + c * 512);
-        w[1][c] = ld_nt(g0 + H + c * 512);
-        w[2][c] = ld_nt(u0 + c * 512);
-        w[3][c] = ld_nt(u0 + H + c * 512);
-    }
-    float acc[4 * NT];
+    for (int c = 0; c < CH; c++) {
 #pragma unroll
-    for (int i = 0; i < 4 * NT; i++) acc[i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < chunks; c++) {
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const uint4 xv = ld16(xp + (long)(off + (t < n ? t : 0)) * H + c * 512 + l * 8);
-            const uint4 a = zero_unless(t < n, xv);
-#pragma unroll
-            for (int r = 0; r < 4; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
+        for (int r = 0; r < FR; r++) {
+            w[r][c] = ld_nt(g0 + (long)r * H + c * 512);
+            w[FR + r][c] = ld_nt(u0 + (long)r * H + c * 512);
         }
     }
-    // lane l now owns entry j = l >> shift: row r = j / NT (0,1 gate; 2,3 up), token t = j % NT
-    const float v = wave_transpose_reduce<4 * NT>(acc);
-    constexpr int V = 4 * NT;
-    constexpr int shift = V == 16 ? 2 : V == 32 ? 1 : 0;
-    const float up = __shfl_down(v, (2 * NT) << shift, WAVE);   // entry j + 2*NT: the matching up row
+    // the expert's token rows, once per block, into LDS
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    for (int i = threadIdx.x; i < n * (H / 8); i += blockDim.x)
+        *reinterpret_cast<uint4*>(xs + i * 8) = ld16(xp + (long)off * H + i * 8);
+    __syncthreads();
+    constexpr int V = 2 * FR * NT;
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            uint4 a = make_uint4(0, 0, 0, 0);
+            if (t < n) a = *reinterpret_cast<const uint4*>(xs + t * H + c * 512 + l * 8);
+#pragma unroll
+            for (int r = 0; r < 2 * FR; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
+        }
+    }
+    // lane l now owns entry j = l >> shift: row r = j / NT (< FR: gate, else up), token t = j % NT
+    const float v = wave_transpose_reduce<V>(acc);
+    constexpr int shift = V == 8 ? 3 : V == 16 ? 2 : V == 32 ? 1 : 0;
+    const float up = __shfl_down(v, (FR * NT) << shift, WAVE);   // entry j + FR*NT: the matching up row
     const int j = l >> shift;
     const int r = j / NT, t = j % NT;
-    if ((l & ((1 << shift) - 1)) == 0 && r < 2 && t < n)
+    if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
         abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_s(v) * up);
 }
 
-template <int NT, int YBF16, int FCH>
-__global__ __launch_bounds__(256) void k_down_valu(const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ wd,
-                                                   const int4* __restrict__ list, int H, int F,
-                                                   void* __restrict__ y) {
+// down: a wave owns DR hidden rows over the whole of F; DW waves per block
+// share the expert's A rows in LDS.
+template <int NT, int YBF16, int FCH, int DR, int DW>
+__global__ __launch_bounds__(64 * DW) void k_down_valu(const uint16_t* __restrict__ abuf,
+                                                       const uint16_t* __restrict__ wd, const int4* __restrict__ list,
+                                                       int H, int F, void* __restrict__ y) {
     const int4 ent = list[blockIdx.y];
     const int e = ent.x, off = ent.y, n = ent.z;
     if (e < 0) return;
     const int wave = threadIdx.x / WAVE, l = lane_id();
-    const int h0 = (blockIdx.x * 4 + wave) * DV_ROWS;
-    constexpr int chunks = FCH;                 // 1 KB chunks per row: F = 512 * FCH
-    uint4 w[DV_ROWS][FCH];
+    const int h0 = (blockIdx.x * DW + wave) * DR;
+    uint4 w[DR][FCH];
 #pragma unroll
-    for (int c = 0; c < chunks; c++) {
+    for (int c = 0; c < FCH; c++) {
 #pragma unroll
-        for (int r = 0; r < DV_ROWS; r++) w[r][c] = ld_nt(wd + ((long)e * H + h0 + r) * F + c * 512 + l * 8);
+        for (int r = 0; r < DR; r++) w[r][c] = ld_nt(wd + ((long)e * H + h0 + r) * F + c * 512 + l * 8);
     }
-    float acc[DV_ROWS * NT];
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* as = reinterpret_cast<uint16_t*>(smem);
+    for (int i = threadIdx.x; i < n * (F / 8); i += blockDim.x)
+        *reinterpret_cast<uint4*>(as + i * 8) = ld16(abuf + (long)off * F + i * 8);
+    __syncthreads();
+    constexpr int V = DR * NT;
+    float acc[V];
 #pragma unroll
-    for (int i = 0; i < DV_ROWS * NT; i++) acc[i] = 0.f;
+    for (int i = 0; i < V; i++) acc[i] = 0.f;
 #pragma unroll
-    for (int c = 0; c < chunks; c++) {
+    for (int c = 0; c < FCH; c++) {
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            const uint4 av = ld16(abuf + (long)(off + (t < n ? t : 0)) * F + c * 512 + l * 8);
-            const uint4 a = zero_unless(t < n, av);
+            uint4 a = make_uint4(0, 0, 0, 0);
+            if (t < n) a = *reinterpret_cast<const uint4*>(as + t * F + c * 512 + l * 8);
 #pragma unroll
-            for (int r = 0; r < DV_ROWS; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
+            for (int r = 0; r < DR; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
         }
     }
-    constexpr int V = DV_ROWS * NT;
     const float v = wave_transpose_reduce<V>(acc);
-    constexpr int shift = V == 32 ? 1 : 0;      // V = 32 or 64 (NT = 4 or 8)
+    constexpr int shift = V == 8 ? 3 : V == 16 ? 2 : V == 32 ? 1 : 0;
     const int j = l >> shift;
     const int r = j / NT, t = j % NT;
     if ((l & ((1 << shift) - 1)) == 0 && t < n) {
@@ -493,16 +509,50 @@ static void launch_wt(const uint16_t* xp, const void* wg, const void* wu, const 
     }
 }
 
+// Block shapes of the VALU kernels (feature rows per wave, waves per block;
+// hidden rows per wave, waves per block); MOE_SMALL_SHAPE="fr,wv,dr,dw" overrides them
+// for tuning runs.
+struct SmallShape { int fr = 2, wv = 4, dr = 8, dw = 4; };
+static SmallShape small_shape() {
+    static SmallShape sh = [] {
+        SmallShape v;
+        if (const char* e = getenv("MOE_SMALL_SHAPE")) sscanf(e, "%d,%d,%d,%d", &v.fr, &v.wv, &v.dr, &v.dw);
+        return v;
+    }();
+    return sh;
+}
+
+template <int NT, int CH, int FR, int WV>
+static void gu_valu(int slots, int H, int F, const uint16_t* xp, const void* wg, const void* wu, const int4* list,
+                    uint16_t* abuf, hipStream_t st) {
+    hipLaunchKernelGGL((k_gateup_valu<NT, CH, FR, WV>), dim3(F / (FR * WV), slots), dim3(64 * WV), (size_t)NT * H * 2,
+                       st, xp, (const uint16_t*)wg, (const uint16_t*)wu, list, H, F, abuf);
+}
+template <int NT, int YB, int FCH, int DR, int DW>
+static void dn_valu(int slots, int H, int F, const uint16_t* abuf, const void* wd, const int4* list, void* y,
+                    hipStream_t st) {
+    hipLaunchKernelGGL((k_down_valu<NT, YB, FCH, DR, DW>), dim3(H / (DR * DW), slots), dim3(64 * DW),
+                       (size_t)NT * F * 2, st, abuf, (const uint16_t*)wd, list, H, F, y);
+}
+template <int NT, int YB, int FCH>
+static void dn_valu_shape(const SmallShape& sh, int slots, int H, int F, const uint16_t* abuf, const void* wd,
+                          const int4* list, void* y, hipStream_t st) {
+    if (sh.dr == 4 && sh.dw == 4) dn_valu<NT, YB, FCH, 4, 4>(slots, H, F, abuf, wd, list, y, st);
+    else if (sh.dr == 4 && sh.dw == 8) dn_valu<NT, YB, FCH, 4, 8>(slots, H, F, abuf, wd, list, y, st);
+    else if (sh.dr == 8 && sh.dw == 8) dn_valu<NT, YB, FCH, 8, 8>(slots, H, F, abuf, wd, list, y, st);
+    else dn_valu<NT, YB, FCH, 8, 4>(slots, H, F, abuf, wd, list, y, st);
+}
+
 template <int NT, int CH, int FCH>
 static void launch_valu(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
                         int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
-    dim3 gg(F / (2 * GV_WAVES), slots), gd(H / (4 * DV_ROWS), slots);
-    hipLaunchKernelGGL((k_gateup_valu<NT, CH>), gg, dim3(64 * GV_WAVES), 0, st, xp, (const uint16_t*)wg,
-                       (const uint16_t*)wu, list, H, F, abuf);
-    if (y_bf16)
-        hipLaunchKernelGGL((k_down_valu<NT, 1, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, list, H, F, y);
-    else
-        hipLaunchKernelGGL((k_down_valu<NT, 0, FCH>), gd, dim3(256), 0, st, abuf, (const uint16_t*)wd, list, H, F, y);
+    const SmallShape sh = small_shape();
+    if (sh.fr == 1 && sh.wv == 4) gu_valu<NT, CH, 1, 4>(slots, H, F, xp, wg, wu, list, abuf, st);
+    else if (sh.fr == 1 && sh.wv == 8) gu_valu<NT, CH, 1, 8>(slots, H, F, xp, wg, wu, list, abuf, st);
+    else if (sh.fr == 2 && sh.wv == 8) gu_valu<NT, CH, 2, 8>(slots, H, F, xp, wg, wu, list, abuf, st);
+    else gu_valu<NT, CH, 2, 4>(slots, H, F, xp, wg, wu, list, abuf, st);
+    if (y_bf16) dn_valu_shape<NT, 1, FCH>(sh, slots, H, F, abuf, wd, list, y, st);
+    else dn_valu_shape<NT, 0, FCH>(sh, slots, H, F, abuf, wd, list, y, st);
 }
 
 template <int NT, int CH>
