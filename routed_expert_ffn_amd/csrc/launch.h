@@ -32,6 +32,13 @@ hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const vo
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                             hipStream_t st);
 
+// ffn_gemm.hip (many rows per expert; bf16 weights)
+bool ffn_gemm_eligible(int H, int F);
+size_t ffn_gemm_workspace_bytes(int T, int K, int E, int H, int F);
+hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                           const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
+                           hipStream_t st);
+
 // combine.hip
 hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w, const void* res, int T,
                           int K, int H, void* out, int out_bf16, hipStream_t st);
