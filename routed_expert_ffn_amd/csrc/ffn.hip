@@ -343,7 +343,7 @@ size_t ffn_workspace_bytes(int T, int K, int E, int H, int F, int x_dtype, int w
         const size_t s = ffn_small_workspace_bytes(T, K, E, H, F);
         b = s > b ? s : b;
     }
-    if (x_dtype != DT_F32 && ffn_gemm_eligible(H, F)) {
+    if (x_dtype != DT_F32 && ffn_gemm_eligible(T, K, H, F)) {
         const size_t s = ffn_gemm_workspace_bytes(T, K, E, H, F);
         b = s > b ? s : b;
     }
@@ -367,7 +367,7 @@ hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, c
     if (ffn_small_eligible(T, H, F))
         return launch_ffn_small(x, w_dtype, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y,
                                 y_dtype == DT_BF16, ws, st);
-    if (w_dtype == DT_BF16 && ffn_gemm_eligible(H, F))
+    if (w_dtype == DT_BF16 && ffn_gemm_eligible(T, K, H, F))
         return launch_ffn_gemm(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_dtype == DT_BF16, ws, st);
     uint16_t* abuf = (uint16_t*)ws;
     const int tiles_g = (n + G_BM - 1) / G_BM + (E < n ? E : n);

@@ -6,20 +6,25 @@
 // (expert = gate/up/down matrices, "Strata Coder 编程模型深度剖析" §3).
 //
 // MFMA-bound at prefill (an 8192-token chunk is ~465 flop per weight byte),
-// so the kernel is built around the bf16 MFMA 16x16x32:
-//   * block tile 128 rows x 256 columns, K step 64; 4 waves, each 64 x 128 (32
-//     MFMA tiles, 128 fp32 accumulators), which keeps LDS reads at ~75% of the
-//     MFMA time;
-//   * global -> LDS with the gfx950 LDS DMA (global_load_lds_dwordx4): no VGPR
-//     staging, three LDS stages (3 x 48 KB) so two K steps of loads are in
-//     flight while one is multiplied;
+// so the kernel is built around the bf16 MFMA 16x16x32 with one wave per SIMD:
+//   * block tile BM x BN (256 x 256 or 128 x 512), K step 64; each of the 4
+//     waves owns a 128 x 128 sub-tile (64 MFMA tiles, 256 fp32 accumulators),
+//     the largest a wave can hold, which minimises LDS operand traffic per MFMA;
+//   * global -> LDS with the gfx950 LDS DMA (global_load_lds_dwordx4), two LDS
+//     stages; the operand fragments are prefetched from LDS into registers one
+//     half-step ahead, so LDS reads and the next stage's DMA both run under the
+//     MFMAs and one barrier per K step suffices;
 //   * LDS rows are 128 B with the 16-byte chunks XOR-swizzled by (row & 7), so
 //     the MFMA operand reads (16 rows x 16 B per lane group) hit distinct
 //     banks; the swizzle is applied on the global side of the DMA;
-//   * gate/up: the 256 B-rows of a block are, per wave half, 64 gate rows then
-//     the same 64 up rows, so silu(g)*u meets in one lane's accumulators;
+//   * the MFMA is issued with the weight fragment as its first operand, so a
+//     lane's accumulators are 4 consecutive output columns of one row: the
+//     epilogue packs them to bf16 and stages each wave's tile through LDS for
+//     16-byte row-contiguous global stores;
+//   * gate/up: the 128 B-rows of a wave are 64 gate rows then the same 64 up
+//     rows, so silu(g)*u meets in one lane's accumulators;
 //   * the activation rows are gathered through perm in the DMA addresses;
-//   * a plan kernel lists every (expert, 128-row tile); blocks map to
+//   * a plan kernel lists every (expert, BM-row tile); blocks map to
 //     (m-tile, n-tile) with n fastest, and consecutive work items are kept on
 //     one XCD (blocks are dealt round-robin over the 8 XCDs) so the tiles that
 //     share weights and activation rows share an L2.
@@ -28,14 +33,24 @@
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int STAGES = 3;
-constexpr int A_BYTES = BM * BK * 2;          // 16 KB
-constexpr int B_BYTES = BN * BK * 2;          // 32 KB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int DMA_A = A_BYTES / 1024 / 4;     // 1 KB DMA instructions per wave per stage (A)
-constexpr int DMA_B = B_BYTES / 1024 / 4;     // (B)
-constexpr int DMA_PER_STAGE = DMA_A + DMA_B;  // 12
+constexpr int BK = 64;
+constexpr int NWAVE = 4;
+
+template <int BM, int BN>
+struct Geo {
+    static constexpr int WM = BM / 128, WN = BN / 128;      // waves along rows / columns
+    static_assert(WM * WN == NWAVE, "4 waves of 128 x 128");
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BN * BK * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int DMA_A = A_BYTES / 1024 / NWAVE;     // 1 KB DMA instructions per wave per stage
+    static constexpr int DMA_B = B_BYTES / 1024 / NWAVE;
+    static constexpr int DMA = DMA_A + DMA_B;
+    static constexpr int LDS = 2 * STAGE;
+    // the epilogue stages each wave's tile through a quarter of stage 1
+    static_assert(STAGE / NWAVE >= 128 * 144 && STAGE / NWAVE >= 64 * 272 && STAGE / NWAVE >= 32 * 528,
+                  "epilogue staging fits a quarter stage");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -43,19 +58,32 @@ MOE_DEV void dma16(const void* g, lds_void* l) {
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
 
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+// s_waitcnt vmcnt(N) / lgkmcnt(0), the other counters left alone (gfx9 encoding)
 template <int N>
 MOE_DEV void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+MOE_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-MOE_DEV float silu_g(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware exp and reciprocal (~1 ulp each;
+// the product is rounded to bf16 right after)
+MOE_DEV float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (round to nearest even, one v_cvt_pk_bf16_f32)
+MOE_DEV uint32_t cvt_bf16x2(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
-// Plan: tiles[i] = (expert, first row, rows) for every 128-row tile of every
+// Plan: tiles[i] = (expert, first row, rows) for every bm-row tile of every
 // touched expert, in expert order; tiles_count[0] = their number.
-__global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ offsets, int E,
+__global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ offsets, int E, int bm,
                                                    int4* __restrict__ tiles, int32_t* __restrict__ count) {
     __shared__ int wave_tot[4];
     __shared__ int s_base;
@@ -65,7 +93,7 @@ __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ o
         const int e = e0 + threadIdx.x;
         int off = 0, n = 0;
         if (e < E) { off = offsets[e]; n = offsets[e + 1] - off; }
-        const int t = (n + BM - 1) / BM;
+        const int t = (n + bm - 1) / bm;
         const int incl = wave_incl_scan(t);
         const int w = threadIdx.x / WAVE;
         if (lane_id() == WAVE - 1) wave_tot[w] = incl;
@@ -73,7 +101,7 @@ __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ o
         int before = s_base;
         for (int i = 0; i < w; i++) before += wave_tot[i];
         const int start = before + incl - t;
-        for (int j = 0; j < t; j++) tiles[start + j] = make_int4(e, off + j * BM, min(BM, n - j * BM), 0);
+        for (int j = 0; j < t; j++) tiles[start + j] = make_int4(e, off + j * bm, min(bm, n - j * bm), 0);
         __syncthreads();
         if (threadIdx.x == 255) s_base = start + t;
         __syncthreads();
@@ -81,162 +109,350 @@ __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ o
     if (threadIdx.x == 0) count[0] = s_base;
 }
 
-template <int PHASE, int YBF16>   // PHASE 0: gate/up (K = H), 1: down (K = F)
+template <int BM, int BN, int PHASE, int YBF16>   // PHASE 0: gate/up (K = H), 1: down (K = F)
 __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, const uint16_t* __restrict__ w0,
                                               const uint16_t* __restrict__ w1, const int4* __restrict__ tiles,
                                               const int32_t* __restrict__ tile_count, const int32_t* __restrict__ perm,
                                               int topk, int H, int F, void* __restrict__ out) {
+    using G = Geo<BM, BN>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int KD = PHASE == 0 ? H : F;            // reduction length
-    const int NT = PHASE == 0 ? (2 * F) / BN : H / BN;   // n-tiles per m-tile
+    const int KD = PHASE == 0 ? H : F;                       // reduction length
+    const int NT = PHASE == 0 ? (2 * F) / BN : H / BN;       // n-tiles per m-tile
+    const int nk = KD / BK;
     const int items = tile_count[0] * NT;
-    // XCD-aware work mapping: blocks b = x (mod 8) take a contiguous range of items
+    // persistent blocks, XCD-aware: the blocks of XCD x (= blockIdx mod 8) own
+    // the contiguous item range [x*per_xcd, (x+1)*per_xcd) and walk it with a
+    // stride of their number, so the blocks running together on one XCD work on
+    // neighbouring items (same expert weights, same activation rows) in its L2
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
     const int per_xcd = (items + 7) / 8;
-    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if ((blockIdx.x >> 3) >= per_xcd || item >= items) return;
-    const int4 tl = tiles[item / NT];
-    const int e = tl.x, row0 = tl.y, rows = tl.z;
-    const int nt = item % NT;
+    const int item_end = min(items, (xcd + 1) * per_xcd);
+    int item = xcd * per_xcd + slot;
+    if (item >= item_end) return;
 
-    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), l = lane_id();
+    const int wm = wave / G::WN, wn = wave % G::WN;
 
-    // ---- DMA source rows (per lane: one row for each of this wave's instructions)
-    // an instruction covers 8 rows x 128 B: lane j -> row r0 + j/8, slot j%8 holding chunk (j%8) ^ (row & 7)
+    // ---- DMA source rows: an instruction covers 8 rows x 128 B; lane j -> row
+    // r0 + j/8, LDS slot j%8 holding global chunk (j%8) ^ (row & 7).  Addresses
+    // are a wave-uniform base plus a 32-bit per-lane byte offset.
     const int dma_row = l >> 3, dma_slot = l & 7;
-    const uint16_t* a_src[DMA_A];
+    const unsigned char* src_b = (const unsigned char*)src;
+    // B: the 8 rows of one instruction are consecutive weight rows (and all gate
+    // or all up), so one lane offset serves every instruction
+    const uint32_t b_off = (uint32_t)dma_row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ dma_row) * 16);
+    struct Item { int e, row0, rows, nt; };
+    auto item_of = [&](int it) __attribute__((always_inline)) -> Item {
+        const int4 tl = tiles[it / NT];
+        return Item{tl.x, tl.y, tl.z, it % NT};
+    };
+    uint32_t a_off[G::DMA_A];
+    auto set_a = [&](const Item& c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < DMA_A; i++) {
-        const int r = (wave * DMA_A + i) * 8 + dma_row;
-        const int rr = r < rows ? r : 0;              // rows past the expert's count re-read row 0 (discarded)
-        long base;
-        if constexpr (PHASE == 0) base = (long)(perm[row0 + rr] / topk) * H;
-        else base = (long)(row0 + rr) * F;
-        a_src[i] = src + base + ((dma_slot ^ (r & 7)) * 8);
-    }
-    const uint16_t* b_src[DMA_B];
-#pragma unroll
-    for (int i = 0; i < DMA_B; i++) {
-        const int n = (wave * DMA_B + i) * 8 + dma_row;     // B tile row 0..255
-        long wrow;
-        const uint16_t* wsrc;
-        if constexpr (PHASE == 0) {
-            const int half = n >> 7, q = n & 127;            // wave half, then 64 gate rows + 64 up rows
-            const int f = nt * 128 + half * 64 + (q & 63);
-            wsrc = q < 64 ? w0 : w1;
-            wrow = (long)e * F + f;
-        } else {
-            wsrc = w0;
-            wrow = (long)e * H + nt * BN + n;
+        for (int i = 0; i < G::DMA_A; i++) {
+            const int r = (wave * G::DMA_A + i) * 8 + dma_row;
+            const int rr = r < c.rows ? r : 0;        // rows past the tile's count re-read row 0 (discarded)
+            uint32_t row;
+            if constexpr (PHASE == 0) row = (uint32_t)(perm[c.row0 + rr] / topk);
+            else row = (uint32_t)(c.row0 + rr);
+            a_off[i] = row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ (r & 7)) * 16);
         }
-        b_src[i] = wsrc + wrow * KD + ((dma_slot ^ (n & 7)) * 8);
-    }
-    auto issue = [&](int k) __attribute__((always_inline)) {
-        unsigned char* st = smem + (k % STAGES) * STAGE_BYTES;
+    };
+    auto b_base = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
+        const int n0 = (wave * G::DMA_B + i) * 8;               // first B tile row of instruction i
+        if constexpr (PHASE == 0) {
+            const int q = n0 & 127;                              // per 128 rows: 64 gate rows, the same 64 up rows
+            const long f = (long)c.e * F + c.nt * (BN / 2) + (n0 >> 7) * 64 + (q & 63);
+            return (const unsigned char*)(q < 64 ? w0 : w1) + f * KD * 2;
+        } else {
+            return (const unsigned char*)w0 + ((long)c.e * H + c.nt * BN + n0) * KD * 2;
+        }
+    };
+    auto issue = [&](const Item& c, int k) __attribute__((always_inline)) {
+        unsigned char* st = smem + (k & 1) * G::STAGE;
 #pragma unroll
-        for (int i = 0; i < DMA_A; i++)
-            dma16(a_src[i] + k * BK, (lds_void*)(st + (wave * DMA_A + i) * 1024));
+        for (int i = 0; i < G::DMA_A; i++)
+            dma16(src_b + k * BK * 2 + a_off[i], (lds_void*)(st + (wave * G::DMA_A + i) * 1024));
 #pragma unroll
-        for (int i = 0; i < DMA_B; i++)
-            dma16(b_src[i] + k * BK, (lds_void*)(st + A_BYTES + (wave * DMA_B + i) * 1024));
+        for (int i = 0; i < G::DMA_B; i++)
+            dma16(b_base(c, i) + k * BK * 2 + b_off, (lds_void*)(st + G::A_BYTES + (wave * G::DMA_B + i) * 1024));
     };
 
-    f32x4_t acc[4][8];
+    // ---- operand fragments of one K half (32) for the 32x32x16 MFMA: 4 row
+    // tiles of A and 4 column tiles of B, each as two K=16 slices
+    const int fr = l & 31, fh = l >> 5;
+    struct Frag { bf16x8_t a[4][2], b[4][2]; };
+    auto load_frag = [&](Frag& fragm, int stage, int kk) __attribute__((always_inline)) {
+        const unsigned char* st = smem + stage * G::STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = KD / BK;
-    issue(0);
-    if (nk > 1) issue(1);
-    // operand read offsets: row within the stage region, swizzled chunk
-    const int fr = l & 15, fg = l >> 4;
-    for (int k = 0; k < nk; k++) {
-        if (k + 1 < nk) wait_vmcnt<DMA_PER_STAGE>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (k + 2 < nk) issue(k + 2);
-        const unsigned char* st = smem + (k % STAGES) * STAGE_BYTES;
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            const int c = kk * 4 + fg;
-            bf16x8_t af[4], bfr[8];
+        for (int q = 0; q < 2; q++) {
+            const int c = kk * 4 + q * 2 + fh;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int r = wm * 64 + i * 16 + fr;
-                af[i] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((c ^ (r & 7)) * 16));
+                const int r = wm * 128 + i * 32 + fr;
+                fragm.a[i][q] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((c ^ (r & 7)) * 16));
             }
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int n = wn * 128 + j * 16 + fr;
-                bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + A_BYTES + n * 128 + ((c ^ (n & 7)) * 16));
+            for (int j = 0; j < 4; j++) {
+                const int n = wn * 128 + j * 32 + fr;
+                fragm.b[j][q] = *reinterpret_cast<const bf16x8_t*>(st + G::A_BYTES + n * 128 + ((c ^ (n & 7)) * 16));
             }
+        }
+    };
+    // acc[i][j][v]: output row i*32 + (l & 31), column j*32 + (v/4)*8 + (l >> 5)*4 + v%4 of the wave tile
+    f32x16_t acc[4][4];
+    auto mma = [&](const Frag& fragm) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 2; q++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fragm.b[j][q], fragm.a[i][q], acc[i][j], 0, 0, 0);
+    };
+    // 16 LDS reads (and, after the barrier, this wave's DMA instructions for
+    // the stage two steps ahead) spread over the 32 MFMAs of a K half
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
         }
-    }
+    };
+    auto interleave_dma = [&]() __attribute__((always_inline)) {
+        static_assert(G::DMA >= 16 && G::DMA <= 32, "1 or 2 DMA instructions per group");
+#pragma unroll
+        for (int q = 0; q < G::DMA - 16; q++) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // 2 VMEM (LDS DMA)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+        }
+#pragma unroll
+        for (int q = G::DMA - 16; q < 16; q++) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (LDS DMA)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+        }
+    };
 
-    // ---- epilogue.  acc[i][j]: rows wm*64 + i*16 + fg*4 + r, column (l & 15) of n-subtile j
+    // ---- epilogue of one item, staged per wave through the LDS of stage 1
+    // (20 KB a wave) while the next item's first stage loads into stage 0
+    auto epilogue = [&](const Item& c) __attribute__((always_inline)) {
+        unsigned char* ep = smem + G::STAGE + wave * (G::STAGE / NWAVE);
+        const int orow0 = wm * 128;                  // wave tile's first row within the block tile
+        if constexpr (PHASE == 0) {
+            // activation: 128 rows x 64 columns bf16, row stride 144 B (18 KB)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int m = wm * 64 + i * 16 + fg * 4 + r;
-            if (m >= rows) continue;
-            const long prow = row0 + m;
-            if constexpr (PHASE == 0) {
+                for (int j = 0; j < 2; j++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int f = nt * 128 + wn * 64 + j * 16 + fr;
-                    const float a = silu_g(acc[i][j][r]) * acc[i][j + 4][r];
-                    ((uint16_t*)out)[prow * F + f] = f32_to_bf16_rne(a);
+                    for (int g = 0; g < 4; g++) {
+                        u32x2_t v;
+                        const f32x16_t& ga = acc[i][j];
+                        const f32x16_t& ua = acc[i][j + 2];
+                        v[0] = cvt_bf16x2(silu_fast(ga[g * 4 + 0]) * ua[g * 4 + 0], silu_fast(ga[g * 4 + 1]) * ua[g * 4 + 1]);
+                        v[1] = cvt_bf16x2(silu_fast(ga[g * 4 + 2]) * ua[g * 4 + 2], silu_fast(ga[g * 4 + 3]) * ua[g * 4 + 3]);
+                        *reinterpret_cast<u32x2_t*>(ep + (i * 32 + fr) * 144 + (j * 32 + g * 8 + fh * 4) * 2) = v;
+                    }
+            wait_lgkm0();
+            __builtin_amdgcn_wave_barrier();
+            uint16_t* A = (uint16_t*)out;
+            const int fc0 = c.nt * (BN / 2) + wn * 64;
+#pragma unroll
+            for (int it = 0; it < 16; it++) {        // 8 lanes x 16 B per row, 8 rows per instruction
+                const int r = it * 8 + (l >> 3), cc = l & 7;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r * 144 + cc * 16);
+                const int m = orow0 + r;
+                if (m < c.rows) *reinterpret_cast<u32x4_t*>(A + (long)(c.row0 + m) * F + fc0 + cc * 8) = v;
+            }
+        } else if constexpr (YBF16) {
+            // two passes of 64 rows x 128 columns bf16, row stride 272 B (17 KB)
+            uint16_t* Y = (uint16_t*)out;
+            const int h0 = c.nt * BN + wn * 128;
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+#pragma unroll
+                        for (int g = 0; g < 4; g++) {
+                            const f32x16_t& a = acc[half * 2 + i][j];
+                            u32x2_t v;
+                            v[0] = cvt_bf16x2(a[g * 4 + 0], a[g * 4 + 1]);
+                            v[1] = cvt_bf16x2(a[g * 4 + 2], a[g * 4 + 3]);
+                            *reinterpret_cast<u32x2_t*>(ep + (i * 32 + fr) * 272 + (j * 32 + g * 8 + fh * 4) * 2) = v;
+                        }
+                wait_lgkm0();
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int it = 0; it < 16; it++) {    // 16 lanes x 16 B per row, 4 rows per instruction
+                    const int r = it * 4 + (l >> 4), cc = l & 15;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r * 272 + cc * 16);
+                    const int m = orow0 + half * 64 + r;
+                    if (m < c.rows) *reinterpret_cast<u32x4_t*>(Y + (long)(c.row0 + m) * H + h0 + cc * 8) = v;
                 }
-            } else {
+                wait_lgkm0();
+                __builtin_amdgcn_wave_barrier();
+            }
+        } else {
+            // four passes of 32 rows x 128 columns fp32, row stride 528 B (16.5 KB)
+            float* Y = (float*)out;
+            const int h0 = c.nt * BN + wn * 128;
 #pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const int h = nt * BN + wn * 128 + j * 16 + fr;
-                    if constexpr (YBF16) ((uint16_t*)out)[prow * H + h] = f32_to_bf16_rne(acc[i][j][r]);
-                    else ((float*)out)[prow * H + h] = acc[i][j][r];
+            for (int i = 0; i < 4; i++) {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        const f32x16_t& a = acc[i][j];
+                        *reinterpret_cast<f32x4_t*>(ep + fr * 528 + (j * 32 + g * 8 + fh * 4) * 4) =
+                            f32x4_t{a[g * 4 + 0], a[g * 4 + 1], a[g * 4 + 2], a[g * 4 + 3]};
+                    }
+                wait_lgkm0();
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int it = 0; it < 16; it++) {    // 32 lanes x 16 B per row, 2 rows per instruction
+                    const int r = it * 2 + (l >> 5), cc = l & 31;
+                    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ep + r * 528 + cc * 16);
+                    const int m = orow0 + i * 32 + r;
+                    if (m < c.rows) *reinterpret_cast<f32x4_t*>(Y + (long)(c.row0 + m) * H + h0 + cc * 4) = v;
                 }
+                wait_lgkm0();
+                __builtin_amdgcn_wave_barrier();
             }
         }
+    };
+
+    Item cur = item_of(item);
+    set_a(cur);
+    issue(cur, 0);
+    if (nk > 1) issue(cur, 1);
+    Frag f0, f1;
+    // steady state of one item: the first K half multiplies f0 while the second
+    // half of this stage is read into f1; then, once stage k+1 has landed
+    // everywhere, the DMA of k+2 goes into the drained stage and f0 is refilled
+    // from k+1 under the second half's MFMAs.  The last two steps are peeled so
+    // the loop body has no branches.
+    auto step = [&](int k, bool more) __attribute__((always_inline)) {
+        const int s = k & 1;
+        load_frag(f1, s, 1);
+        mma(f0);
+        interleave();
+        wait_vmcnt<0>();           // this wave's DMA of stage k+1 has landed
+        wait_lgkm0();              // and its reads of stage k are done
+        __builtin_amdgcn_s_barrier();
+        if (more) issue(cur, k + 2);   // into the stage just drained
+        load_frag(f0, s ^ 1, 0);
+        mma(f1);
+        if (more) interleave_dma();
+        else interleave();
+    };
+    for (;;) {
+        if (nk > 1) wait_vmcnt<G::DMA>();   // this wave's stage 0 has landed (stage 1 may be in flight)
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+        load_frag(f0, 0, 0);
+        int k = 0;
+        for (; k + 2 < nk; k++) step(k, true);
+        if (k + 1 < nk) { step(k, false); k++; }
+        load_frag(f1, k & 1, 1);
+        mma(f0);
+        interleave();
+        // every operand of this item is in registers once f1 has arrived: the
+        // LDS is free for the next item's first stage and this item's epilogue
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        const Item done = cur;
+        item += nslot;
+        const bool more = item < item_end;
+        if (more) {
+            cur = item_of(item);
+            set_a(cur);
+            issue(cur, 0);
+        }
+        mma(f1);
+        epilogue(done);
+        if (!more) break;
+        __builtin_amdgcn_s_barrier();       // every wave is done with its staging area (stage 1)
+        if (nk > 1) issue(cur, 1);
     }
 }
 
-bool ffn_gemm_eligible(int H, int F) { return H % BN == 0 && H % BK == 0 && (2 * F) % BN == 0 && F % BK == 0; }
+namespace {
+// tile shape per phase: 128 x 512 keeps the row padding of small experts at
+// most 127 rows per expert; both shapes read 128 KB of LDS operands per K step.
+constexpr int GU_BM = 128, GU_BN = 512;
+constexpr int DN_BM = 128, DN_BN = 512;
+constexpr int PLAN_BM = 128;
+static_assert(GU_BM == PLAN_BM && DN_BM == PLAN_BM, "one tile plan serves both phases");
+}  // namespace
 
-// Workspace: [A n x F bf16][tiles: (n/BM + min(E,n)) x int4][count]
+// Shapes the tiles cover exactly; the DMA addresses are 32-bit byte offsets
+// into the activation rows (T x H) and the intermediate (T*K x F).
+bool ffn_gemm_eligible(int T, int K, int H, int F) {
+    return H % DN_BN == 0 && H % BK == 0 && (2 * F) % GU_BN == 0 && F % BK == 0 &&
+           (size_t)T * H * 2 < ((size_t)1 << 32) && (size_t)T * K * F * 2 < ((size_t)1 << 32);
+}
+
+// Workspace: [A n x F bf16][tiles: (n/BM + min(E,n) + 1) x int4][count]
 size_t ffn_gemm_workspace_bytes(int T, int K, int E, int H, int F) {
     (void)H;
     const size_t n = (size_t)T * K;
-    const size_t mt = n / BM + (size_t)(E < (int)n ? E : (int)n) + 1;
+    const size_t mt = n / PLAN_BM + (size_t)(E < (int)n ? E : (int)n) + 1;
     return (n * F * 2 + 255) / 256 * 256 + (mt * 16 + 255) / 256 * 256 + 256;
+}
+
+template <int BM, int BN, int PHASE, int YBF16>
+static hipError_t launch_one(int items, hipStream_t st, const uint16_t* src, const uint16_t* w0, const uint16_t* w1,
+                             const int4* tiles, const int32_t* count, const int32_t* perm, int K, int H, int F,
+                             void* out) {
+    auto kern = k_gemm<BM, BN, PHASE, YBF16>;
+    const int lds = Geo<BM, BN>::LDS;
+    static bool attr = false;     // raising the dynamic LDS limit is per function, once
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    // persistent: one block per CU (the LDS holds one), a multiple of the 8 XCDs
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int cap = ncu / 8 * 8 > 8 ? ncu / 8 * 8 : 8;
+    const int grid = (items + 7) / 8 * 8 < cap ? (items + 7) / 8 * 8 : cap;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, src, w0, w1, tiles, count, perm, K, H, F, out);
+    return hipSuccess;
 }
 
 hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
                            const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                            hipStream_t st) {
     const size_t n = (size_t)T * K;
-    const size_t mt = n / BM + (size_t)(E < (int)n ? E : (int)n) + 1;
+    const size_t mt = n / PLAN_BM + (size_t)(E < (int)n ? E : (int)n) + 1;
     char* base = (char*)ws;
     uint16_t* abuf = (uint16_t*)base;
     int4* tiles = (int4*)(base + (n * F * 2 + 255) / 256 * 256);
     int32_t* count = (int32_t*)((char*)tiles + (mt * 16 + 255) / 256 * 256);
-    hipLaunchKernelGGL(k_gemm_plan, dim3(1), dim3(256), 0, st, offsets, E, tiles, count);
-    const size_t lds = (size_t)STAGES * STAGE_BYTES;
-    const int items_g = (int)mt * ((2 * F) / BN), items_d = (int)mt * (H / BN);
-    const int grid_g = (items_g + 7) / 8 * 8, grid_d = (items_d + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_gemm<0, 1>), dim3(grid_g), dim3(256), lds, st, (const uint16_t*)x, (const uint16_t*)wg,
-                       (const uint16_t*)wu, tiles, count, perm, K, H, F, (void*)abuf);
+    hipLaunchKernelGGL(k_gemm_plan, dim3(1), dim3(256), 0, st, offsets, E, PLAN_BM, tiles, count);
+    const int items_g = (int)mt * ((2 * F) / GU_BN), items_d = (int)mt * (H / DN_BN);
+    hipError_t e = launch_one<GU_BM, GU_BN, 0, 1>(items_g, st, (const uint16_t*)x, (const uint16_t*)wg,
+                                                  (const uint16_t*)wu, tiles, count, perm, K, H, F, abuf);
+    if (e != hipSuccess) return e;
     if (y_bf16)
-        hipLaunchKernelGGL((k_gemm<1, 1>), dim3(grid_d), dim3(256), lds, st, (const uint16_t*)abuf,
-                           (const uint16_t*)wd, nullptr, tiles, count, perm, K, H, F, y);
+        e = launch_one<DN_BM, DN_BN, 1, 1>(items_d, st, abuf, (const uint16_t*)wd, nullptr, tiles, count, perm, K,
+                                           H, F, y);
     else
-        hipLaunchKernelGGL((k_gemm<1, 0>), dim3(grid_d), dim3(256), lds, st, (const uint16_t*)abuf,
-                           (const uint16_t*)wd, nullptr, tiles, count, perm, K, H, F, y);
+        e = launch_one<DN_BM, DN_BN, 1, 0>(items_d, st, abuf, (const uint16_t*)wd, nullptr, tiles, count, perm, K,
+                                           H, F, y);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -74,6 +74,10 @@ SMALL = [
     synth.LayerShape(T=300, H=256, E=40, K=6, F=128, act="bf16", wdt="int4", zipf=True),
     synth.LayerShape(T=77, H=384, E=100, K=10, F=192, act="bf16", wdt="bf16"),
     synth.LayerShape(T=130, H=128, E=8, K=8, F=64, act="bf16", wdt="int4"),
+    # bf16 weights, H and 2F multiples of 512: the grouped-GEMM path (128-row
+    # tiles, ragged last tile per expert, one item per block)
+    synth.LayerShape(T=300, H=512, E=40, K=6, F=256, act="bf16", wdt="bf16", zipf=True),
+    synth.LayerShape(T=97, H=1024, E=12, K=3, F=512, act="bf16", wdt="bf16"),
     # T <= 16: the weight-streaming path for the verify step
     synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="bf16", zipf=True),
     synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="int4", zipf=True),
@@ -103,6 +107,24 @@ def test_small_layers_span_tiles(s):
     # fp32 y_perm gives the same routing and an in-tolerance output
     out32, _ = run_layer(d, y_dtype=torch.float32)
     assert row_rel_err(to_host(out32), ref_out) <= TOL_BF16
+
+
+def test_gemm_path_blocks_walk_several_items():
+    """More 128-row tiles than the chip has CUs: every persistent block of the
+    grouped GEMM handles several (expert, tile) items in turn."""
+    s = synth.LayerShape(T=4096, H=1024, E=16, K=8, F=512, act="bf16", wdt="bf16", zipf=True)
+    h = synth.make_host_layer(s, seed=5, cfg=7)
+    d = device_from_host(h)
+    ref_idx, ref_w, _ = oracle.route(h.x, h.wr, s.K, h.bias)
+    counts = np.bincount(ref_idx.ravel(), minlength=s.E)
+    items_per_phase = int(np.sum((counts + 127) // 128)) * 2
+    assert items_per_phase > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    rows = np.unique(np.concatenate([[0, s.T - 1], np.random.default_rng(1).choice(s.T, 62, replace=False)]))
+    ref_out = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d), rows=rows)
+    for y_dtype in (None, torch.float32):
+        out, r = run_layer(d, y_dtype=y_dtype)
+        check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+        assert row_rel_err(to_host(out)[rows], ref_out) <= TOL_BF16
 
 
 # ---------------------------------------------------------------- routing edge cases
