@@ -17,8 +17,10 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 hipStream_t S(moe_stream s) { return (hipStream_t)s; }
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-bool fast_route_eligible(int T, int H, int x_dtype, const void* x, const float* logits_out) {
-    return x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && H % 32 == 0 && logits_out == nullptr && aligned16(x);
+bool fast_route_eligible(int T, int H, int E, int x_dtype, const void* x, const float* w_router,
+                         const float* logits_out) {
+    return x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && logits_fast_eligible(T, H, E) && logits_out == nullptr &&
+           aligned16(x) && aligned16(w_router);
 }
 
 }  // namespace
@@ -38,11 +40,31 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-// Workspace: [T][E] fp32 logits, then [T] int32 flags (1 = token re-decided on exact logits).
+// Workspace: [T][E] fp32 logits, [T] int32 flags (1 = token re-decided on
+// exact logits), the recheck queue (a counter, then [T] (token, cut) pairs),
+// and (bf16 activations, many tokens) the router weight split into three
+// bf16 planes for the estimate.
+namespace {
+struct RouteWs {
+    size_t flags, count, list, planes, total;
+};
+RouteWs route_ws_layout(int T, int H, int E, int x_dtype) {
+    RouteWs w;
+    w.flags = round256((size_t)T * E * sizeof(float));
+    w.count = w.flags + round256((size_t)T * sizeof(int32_t));
+    w.list = w.count + 256;
+    w.planes = w.list + round256((size_t)T * 8);
+    w.total = w.planes;
+    if (x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && logits_fast_eligible(T, H, E))
+        w.total += round256(logits_fast_planes_bytes(H, E));
+    return w;
+}
+}  // namespace
+
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype) {
-    (void)H; (void)K; (void)x_dtype;
-    if (T < 0 || E <= 0) return 0;
-    return round256((size_t)T * E * sizeof(float)) + round256((size_t)T * sizeof(int32_t)) + 256;
+    (void)K;
+    if (T < 0 || E <= 0 || H <= 0) return 0;
+    return route_ws_layout(T, H, E, x_dtype).total;
 }
 
 moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T, int32_t H,
@@ -57,19 +79,26 @@ moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, cons
     if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
     hipStream_t st = S(stream);
-    float* lg = (float*)workspace;
-    int32_t* flags = (int32_t*)((char*)workspace + round256((size_t)T * E * sizeof(float)));
+    const RouteWs L = route_ws_layout(T, H, E, x_dtype);
+    char* wb = (char*)workspace;
+    float* lg = (float*)wb;
+    int32_t* flags = (int32_t*)(wb + L.flags);
+    int32_t* rc_count = (int32_t*)(wb + L.count);
+    int2* rc_list = (int2*)(wb + L.list);
     const int xb = x_dtype == MOE_BF16;
     hipError_t err;
-    if (fast_route_eligible(T, H, x_dtype, x, logits_out)) {
-        err = launch_logits_fast((const uint16_t*)x, w_router, bias, T, H, E, lg, st);
+    if (fast_route_eligible(T, H, E, x_dtype, x, w_router, logits_out)) {
+        err = launch_logits_fast((const uint16_t*)x, w_router, bias, T, H, E, lg, (uint16_t*)(wb + L.planes),
+                                 rc_count, st);
         if (err != hipSuccess) return MOE_ERR_HIP;
-        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, topk_idx, topk_w, flags, st);
+        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, topk_idx, topk_w, flags,
+                                  rc_list, rc_count, st);
     } else {
         float* dst = logits_out ? logits_out : lg;
         err = launch_logits_exact(x, xb, w_router, bias, T, H, E, dst, st);
         if (err != hipSuccess) return MOE_ERR_HIP;
-        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, topk_idx, topk_w, flags, st);
+        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, topk_idx, topk_w, flags, rc_list,
+                                  rc_count, st);
     }
     return hip_status(err);
 }

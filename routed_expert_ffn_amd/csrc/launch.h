@@ -7,11 +7,17 @@
 // route.hip
 hipError_t launch_logits_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
                                float* logits, hipStream_t st);
+bool logits_fast_eligible(int T, int H, int E);
+size_t logits_fast_planes_bytes(int H, int E);
+// the estimate (three-plane bf16 split of the router, then the MFMA GEMM); the
+// split kernel also clears *rc_count, the recheck queue's counter
 hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, hipStream_t st);
+                              float* logits, uint16_t* planes, int32_t* rc_count, hipStream_t st);
+// selection; with estimates (exact == 0) tokens within tau are queued in
+// rc_list / rc_count and re-decided on exact logits by a second kernel
 hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
                                int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                               int32_t* n_rechecked, hipStream_t st);
+                               int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st);
 
 // permute.hip
 constexpr int PERM_CHUNK = 2048;   // slots per grouping block

@@ -47,6 +47,48 @@ MOE_DEV double wave_dot_exact(const XT* __restrict__ xrow, const float* __restri
     return p;
 }
 
+// Up to four exact logit dot products of one token row by a whole wave, with
+// the same per-lane order and butterfly as wave_dot_exact; the loads of an
+// 8-term slice of every candidate are issued together (the recheck of a
+// near-tie is latency-bound otherwise).  Results for c >= nc are meaningless.
+template <typename XT>
+MOE_DEV void wave_dot_exact4(const XT* __restrict__ xrow, const float* __restrict__ wr, const int (&ce)[4], int nc,
+                             int H, double (&out)[4]) {
+    constexpr int U = 8;
+    const int l = lane_id();
+    // every load is unconditional (a predicated load would serialise on its
+    // wait): past-the-end terms re-read element H-1 and are not accumulated,
+    // absent candidates re-read the first
+    const float* wrow[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) wrow[c] = wr + (long)(c < nc ? ce[c] : ce[0]) * H;
+    double p[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int h0 = 0; h0 < H; h0 += WAVE * U) {
+        double xv[U];
+        float wv[4][U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int h = min(h0 + u * WAVE + l, H - 1);
+            xv[u] = xval(xrow, h);
+#pragma unroll
+            for (int c = 0; c < 4; c++) wv[c][u] = wrow[c][h];
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (h0 + u * WAVE + l < H) {
+#pragma unroll
+                for (int c = 0; c < 4; c++) p[c] = __fma_rn(xv[u], (double)wv[c][u], p[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) p[c] += __shfl_xor(p[c], d, WAVE);
+        out[c] = p[c];
+    }
+}
+
 constexpr int EXACT_TPG = 4;   // tokens per register group
 
 template <typename XT>
@@ -90,101 +132,217 @@ __global__ __launch_bounds__(256) void k_logits_exact(const XT* __restrict__ x, 
 
 // ------------------------------------------------------------------ fast logits (bf16 x, 3-term split MFMA)
 
-// Block tile 64 tokens x 64 experts, K step 32; 4 waves as 2x2 of 32x32.
-constexpr int FL_BM = 64, FL_BN = 64, FL_BK = 32, FL_LD = FL_BK + 8;
+// The router weight split once per call: w = hi + mid + lo exactly, each a
+// bf16 (8 significant bits each cover fp32's 24), stored as three planes
+// [3][E][H] so the estimate is a plain bf16 GEMM of x against all three.
+// Thread 0 also clears the recheck queue's counter for the selection that follows.
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ wr, long n4,
+                                                      uint16_t* __restrict__ planes, long plane_elems,
+                                                      int32_t* __restrict__ rc_count) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i == 0) rc_count[0] = 0;
+    if (i >= n4) return;
+    const float4 wv = reinterpret_cast<const float4*>(wr)[i];
+    const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
+    uint32_t hi[2], mi[2], lo[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        uint16_t h16[2], m16[2], l16[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const float w = w4[q * 2 + u];
+            h16[u] = f32_to_bf16_rne(w);
+            const float r1 = w - bf16_to_f32(h16[u]);
+            m16[u] = f32_to_bf16_rne(r1);
+            const float r2 = r1 - bf16_to_f32(m16[u]);
+            l16[u] = f32_to_bf16_rne(r2);
+        }
+        hi[q] = h16[0] | ((uint32_t)h16[1] << 16);
+        mi[q] = m16[0] | ((uint32_t)m16[1] << 16);
+        lo[q] = l16[0] | ((uint32_t)l16[1] << 16);
+    }
+    reinterpret_cast<uint2*>(planes)[i] = make_uint2(hi[0], hi[1]);
+    reinterpret_cast<uint2*>(planes + plane_elems)[i] = make_uint2(mi[0], mi[1]);
+    reinterpret_cast<uint2*>(planes + 2 * plane_elems)[i] = make_uint2(lo[0], lo[1]);
+}
 
-__global__ __launch_bounds__(256) void k_logits_fast(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+// Estimate GEMM: block tile 128 tokens x 128 experts, K step 64, two LDS stages
+// filled by the LDS DMA (rows of 128 B, 16-byte chunks XOR-swizzled by row & 7);
+// 4 waves as 2 x 2 of 64 x 64 on the 32x32x16 MFMA, the three weight planes
+// multiplied against the same activation fragments into one accumulator.
+namespace {
+constexpr int LM_BM = 128, LM_BN = 128, LM_BK = 64;
+constexpr int LM_A = LM_BM * LM_BK * 2;                  // 16 KB
+constexpr int LM_B = LM_BN * LM_BK * 2;                  // 16 KB per plane
+constexpr int LM_STAGE = LM_A + 3 * LM_B;                // 64 KB
+constexpr int LM_DMA_A = LM_A / 1024 / 4, LM_DMA_B = 3 * LM_B / 1024 / 4;   // 4 + 12 per wave
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <int N>
+MOE_DEV void lm_wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+MOE_DEV void lm_wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
                                                      const float* __restrict__ bias, int T, int H, int E,
                                                      float* __restrict__ logits) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[FL_BM * FL_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[3][FL_BN * FL_LD];
-    const int tid = threadIdx.x;
-    const int wave = tid / WAVE, l = lane_id();
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int mt = (T + LM_BM - 1) / LM_BM, ntl = (E + LM_BN - 1) / LM_BN;
+    const int items = mt * ntl;
+    // consecutive items (the n-tiles of one token tile) stay on one XCD
+    const int per_xcd = (items + 7) / 8;
+    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per_xcd || item >= items) return;
+    const int m0 = (item / ntl) * LM_BM, n0 = (item % ntl) * LM_BN;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), l = lane_id();
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.x * FL_BM, n0 = blockIdx.y * FL_BN;
-
-    f32x4_t acc[2][2];
+    const int dma_row = l >> 3, dma_slot = l & 7;
+    const unsigned char* xb = (const unsigned char*)x;
+    const unsigned char* pb = (const unsigned char*)planes;
+    uint32_t a_off[LM_DMA_A];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < LM_DMA_A; i++) {
+        const int r = (wave * LM_DMA_A + i) * 8 + dma_row;
+        const int t = m0 + r < T ? m0 + r : m0;          // rows past T re-read the first (discarded)
+        a_off[i] = (uint32_t)t * (uint32_t)(H * 2) + (uint32_t)((dma_slot ^ (r & 7)) * 16);
+    }
+    uint32_t b_off[LM_DMA_B];
 #pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // loaders: A 64 rows x 32 bf16 = 256 x 16B (one per thread);
-    //          B 64 rows x 32 fp32 = 512 x 16B (two per thread)
-    const int a_r = tid >> 2, a_c = (tid & 3) * 8;
-    const int a_t = m0 + a_r;
-    for (int k0 = 0; k0 < H; k0 += FL_BK) {
-        uint4 av = make_uint4(0, 0, 0, 0);
-        if (a_t < T) av = *reinterpret_cast<const uint4*>(x + (long)a_t * H + k0 + a_c);
-        *reinterpret_cast<uint4*>(&As[a_r * FL_LD + a_c]) = av;
+    for (int i = 0; i < LM_DMA_B; i++) {
+        const int q = wave * LM_DMA_B + i;               // 0..47: plane q/16, rows (q%16)*8 ..
+        const int plane = q >> 4, n = (q & 15) * 8 + dma_row;
+        const int e = n0 + n < E ? n0 + n : n0;
+        b_off[i] = ((uint32_t)plane * (uint32_t)E + (uint32_t)e) * (uint32_t)(H * 2) +
+                   (uint32_t)((dma_slot ^ (n & 7)) * 16);
+    }
+    auto issue = [&](int k) __attribute__((always_inline)) {
+        unsigned char* st = smem + (k & 1) * LM_STAGE;
+#pragma unroll
+        for (int i = 0; i < LM_DMA_A; i++)
+            __builtin_amdgcn_global_load_lds(xb + k * LM_BK * 2 + a_off[i], (lds_void_t*)(st + (wave * LM_DMA_A + i) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < LM_DMA_B; i++)
+            __builtin_amdgcn_global_load_lds(pb + k * LM_BK * 2 + b_off[i],
+                                             (lds_void_t*)(st + LM_A + (wave * LM_DMA_B + i) * 1024), 16, 0, 0);
+    };
+    const int fr = l & 31, fh = l >> 5;
+    struct Frag { bf16x8_t a[2][2], b[3][2][2]; };
+    auto load_frag = [&](Frag& f, int stage, int kk) __attribute__((always_inline)) {
+        const unsigned char* st = smem + stage * LM_STAGE;
 #pragma unroll
         for (int q = 0; q < 2; q++) {
-            const int idx = tid + q * 256;
-            const int b_r = idx >> 3, b_c = (idx & 7) * 4;
-            const int e = n0 + b_r;
-            float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < E) wv = *reinterpret_cast<const float4*>(wr + (long)e * H + k0 + b_c);
-            float w4[4] = {wv.x, wv.y, wv.z, wv.w};
-            uint16_t hi[4], mi[4], lo[4];
+            const int c = kk * 4 + q * 2 + fh;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                // exact split: w = hi + mid + lo, each a bf16 (8 significant bits)
-                float w = w4[i];
-                uint16_t h16 = f32_to_bf16_rne(w);
-                float r1 = w - bf16_to_f32(h16);
-                uint16_t m16 = f32_to_bf16_rne(r1);
-                float r2 = r1 - bf16_to_f32(m16);
-                hi[i] = h16; mi[i] = m16; lo[i] = f32_to_bf16_rne(r2);
+            for (int i = 0; i < 2; i++) {
+                const int r = wm * 64 + i * 32 + fr;
+                f.a[i][q] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((c ^ (r & 7)) * 16));
             }
-            uint2 hv = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-            uint2 mv = make_uint2(mi[0] | ((uint32_t)mi[1] << 16), mi[2] | ((uint32_t)mi[3] << 16));
-            uint2 lv = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-            *reinterpret_cast<uint2*>(&Bs[0][b_r * FL_LD + b_c]) = hv;
-            *reinterpret_cast<uint2*>(&Bs[1][b_r * FL_LD + b_c]) = mv;
-            *reinterpret_cast<uint2*>(&Bs[2][b_r * FL_LD + b_c]) = lv;
+#pragma unroll
+            for (int p = 0; p < 3; p++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int n = wn * 64 + j * 32 + fr;
+                    f.b[p][j][q] = *reinterpret_cast<const bf16x8_t*>(st + LM_A + p * LM_B + n * 128 + ((c ^ (n & 7)) * 16));
+                }
         }
-        __syncthreads();
-        bf16x8_t af[2];
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int r = wm * 32 + i * 16 + (l & 15);
-            af[i] = *reinterpret_cast<const bf16x8_t*>(&As[r * FL_LD + (l >> 4) * 8]);
-        }
-#pragma unroll
-        for (int s = 0; s < 3; s++) {
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int c = wn * 32 + j * 16 + (l & 15);
-                bf16x8_t bfv = *reinterpret_cast<const bf16x8_t*>(&Bs[s][c * FL_LD + (l >> 4) * 8]);
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfv, acc[i][j], 0, 0, 0);
-            }
-        }
-        __syncthreads();
-    }
-    // D layout (16x16 tile): lane l holds column l%16, rows (l/16)*4 + 0..3
+    };
+    f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int e = n0 + wn * 32 + j * 16 + (l & 15);
-            if (e >= E) continue;
-            const float b = bias ? bias[e] : 0.0f;
+        for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int t = m0 + wm * 32 + i * 16 + (l >> 4) * 4 + r;
-                if (t < T) logits[(long)t * E + e] = bias ? __fadd_rn(acc[i][j][r], b) : acc[i][j][r];
-            }
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+    auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 2; q++)
+#pragma unroll
+            for (int p = 0; p < 3; p++)
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[p][j][q], f.a[i][q], acc[i][j], 0, 0, 0);
+    };
+    auto interleave = [&]() __attribute__((always_inline)) {   // 16 LDS reads over 24 MFMAs
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+
+    const int nk = H / LM_BK;
+    issue(0);
+    if (nk > 1) {
+        issue(1);
+        lm_wait_vmcnt<LM_DMA_A + LM_DMA_B>();
+    } else {
+        lm_wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    Frag f0, f1;
+    load_frag(f0, 0, 0);
+    auto step = [&](int k, bool more) __attribute__((always_inline)) {
+        const int s = k & 1;
+        load_frag(f1, s, 1);
+        mma(f0);
+        interleave();
+        lm_wait_vmcnt<0>();
+        lm_wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        if (more) issue(k + 2);
+        load_frag(f0, s ^ 1, 0);
+        mma(f1);
+        interleave();
+    };
+    int k = 0;
+    for (; k + 2 < nk; k++) step(k, true);
+    if (k + 1 < nk) { step(k, false); k++; }
+    load_frag(f1, k & 1, 1);
+    mma(f0);
+    mma(f1);
+
+    // acc[i][j][v]: token m0 + wm*64 + i*32 + (l & 31), expert n0 + wn*64 + j*32 + (v/4)*8 + (l>>5)*4 + v%4
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int t = m0 + wm * 64 + i * 32 + fr;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int e = n0 + wn * 64 + j * 32 + g * 8 + fh * 4;
+                float v4[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const float a = acc[i][j][g * 4 + u];
+                    v4[u] = bias ? __fadd_rn(a, bias[min(e + u, E - 1)]) : a;
+                }
+                if (e + 3 < E) {
+                    *reinterpret_cast<float4*>(logits + (long)t * E + e) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; u++)
+                        if (e + u < E) logits[(long)t * E + e + u] = v4[u];
+                }
+            }
+    }
 }
 
 // ------------------------------------------------------------------ selection
 
 constexpr int SEL_CAP = 64;   // candidates re-decided on exact logits (one per lane)
 
-// Top-`rounds` of the keys held by the wave (any layout); lane r receives
-// round r's key.  Selected entries are cleared from k[].
+// Top-`rounds` of the 64-bit keys held by the wave (any layout); lane r
+// receives round r's key.  Selected entries are cleared from k[].
 template <int VPL>
 MOE_DEV unsigned long long select_rounds(unsigned long long (&k)[VPL], int rounds) {
     const int l = lane_id();
@@ -201,32 +359,93 @@ MOE_DEV unsigned long long select_rounds(unsigned long long (&k)[VPL], int round
     return mine;
 }
 
-template <int VPL, typename XT>
+// Wave-wide maximum of a u32, returned wave-uniform: DPP within each row of
+// 16 lanes (quad swaps, half-row and row mirrors), then the four row maxima.
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+MOE_DEV float order_key_value(uint32_t h) { return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h); }
+
+// Top-`rounds` under (value desc, expert asc) of the order keys kv[j] of expert
+// e = lane + 64 j (0 = absent; every finite or infinite logit has a key > 0):
+// lane r < rounds receives round r's key and expert.  Per round: the lane
+// maxima, their wave maximum M, and the lowest expert holding M (lowest j,
+// then lowest lane, by ballot), which is then cleared.
+template <int VPL>
+MOE_DEV void select_top(uint32_t (&kv)[VPL], int rounds, uint32_t& my_key, int& my_e) {
+    const int l = lane_id();
+    my_key = 0;
+    my_e = 0;
+    for (int r = 0; r < rounds; r++) {
+        uint32_t m = kv[0];
+#pragma unroll
+        for (int j = 1; j < VPL; j++) m = max(m, kv[j]);
+        const uint32_t M = wave_max_u32(m);
+        int win = -1;
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            if (win < 0) {
+                const unsigned long long bm = __ballot(kv[j] == M);
+                if (bm) win = (__ffsll((long long)bm) - 1) + j * WAVE;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; j++) kv[j] = (l + j * WAVE == win) ? 0u : kv[j];
+        if (l == r) {
+            my_key = M;
+            my_e = win;
+        }
+    }
+}
+
+// Routing weights of a wave's selection (lane k < K holds the k-th value and
+// id): softmax over the K selected values, written to row t.
+MOE_DEV void write_selection(float sel_v, int sel_i, int K, long t, int32_t* __restrict__ idx_out,
+                             float* __restrict__ w_out) {
+    const int l = lane_id();
+    const float v0 = __shfl(sel_v, 0, WAVE);
+    const float ex = (l < K) ? expf(sel_v - v0) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
+    if (l < K) {
+        idx_out[t * K + l] = sel_i;
+        w_out[t * K + l] = ex / sum;
+    }
+}
+
+// One wave per token.  With exact logits the top K is final.  With estimates,
+// a token whose K+1 leading values are all separated by at least tau is final
+// too; any other token is queued, with its cut (K-th estimate - tau), for
+// k_route_recheck and written there.
+template <int VPL>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ logits, int T, int E, int K,
-                                                      float tau, int exact,
-                                                      const XT* __restrict__ x, const float* __restrict__ wr,
-                                                      const float* __restrict__ bias, int H,
-                                                      int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                                      int32_t* __restrict__ rechecked) {
+                                                      float tau, int exact, int32_t* __restrict__ idx_out,
+                                                      float* __restrict__ w_out, int32_t* __restrict__ rechecked,
+                                                      int2* __restrict__ rc_list, int32_t* __restrict__ rc_count) {
     const int wave = threadIdx.x / WAVE;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int l = lane_id();
     const float* row = logits + (long)t * E;
-
-    float v[VPL];
-    unsigned long long k[VPL];
+    uint32_t kv[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; j++) {
         const int e = l + j * WAVE;
-        v[j] = e < E ? row[e] : 0.f;
-        k[j] = e < E ? route_key(v[j], e) : 0ull;
+        kv[j] = e < E ? f32_order_key(row[e]) : 0u;
     }
     const int rounds = (exact || K == E) ? K : K + 1;
-    unsigned long long sel = select_rounds<VPL>(k, rounds);
-    float sel_v = route_key_value(sel);
-    int sel_i = route_key_index(sel);
-
+    uint32_t key;
+    int sel_i;
+    select_top<VPL>(kv, rounds, key, sel_i);
+    const float sel_v = order_key_value(key);
     bool flagged = false;
     if (!exact) {
         // every gap between consecutive selected values, down to the (K+1)-th, must clear tau
@@ -234,66 +453,73 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
         const bool check = l < K && l + 1 < rounds;
         flagged = __ballot(check && !(sel_v - nxt >= tau)) != 0;
     }
-
-    if (flagged) {
-        // Candidates: every expert whose estimate exceeds the K-th estimate - tau.
-        const float cut = __shfl(sel_v, K - 1, WAVE) - tau;
-        int ncand = 0;
-#pragma unroll
-        for (int j = 0; j < VPL; j++) {
-            const int e = l + j * WAVE;
-            ncand += wave_sum((e < E && v[j] > cut) ? 1 : 0);
-        }
-        const XT* xrow = x + (long)t * H;
-        if (ncand <= SEL_CAP) {
-            unsigned long long ck = 0;      // lane c holds candidate c's exact key
-            int slot = 0;
-#pragma unroll
-            for (int j = 0; j < VPL; j++) {
-                const int e = l + j * WAVE;
-                unsigned long long m = __ballot(e < E && v[j] > cut);
-                while (m) {
-                    const int src = __ffsll((long long)m) - 1;
-                    m &= m - 1;
-                    const int ce = src + j * WAVE;
-                    float lv = (float)wave_dot_exact(xrow, wr + (long)ce * H, H);
-                    if (bias) lv = __fadd_rn(lv, bias[ce]);
-                    if (l == slot) ck = route_key(lv, ce);
-                    slot++;
-                }
-            }
-            unsigned long long c1[1] = {ck};
-            sel = select_rounds<1>(c1, K);
-        } else {
-            // too many near-equal estimates: decide on exact logits of all experts
-            unsigned long long ek[VPL];
-#pragma unroll
-            for (int j = 0; j < VPL; j++) {
-                ek[j] = 0;
-                for (int src = 0; src < WAVE; src++) {
-                    const int ce = src + j * WAVE;
-                    if (ce >= E) break;
-                    float lv = (float)wave_dot_exact(xrow, wr + (long)ce * H, H);
-                    if (bias) lv = __fadd_rn(lv, bias[ce]);
-                    if (l == src) ek[j] = route_key(lv, ce);
-                }
-            }
-            sel = select_rounds<VPL>(ek, K);
-        }
-        sel_v = route_key_value(sel);
-        sel_i = route_key_index(sel);
-    }
     if (rechecked && l == 0) rechecked[t] = flagged ? 1 : 0;
+    if (flagged) {
+        const float cut = __shfl(sel_v, K - 1, WAVE) - tau;
+        if (l == 0) {
+            const int slot = atomicAdd(rc_count, 1);
+            rc_list[slot] = make_int2(t, __float_as_int(cut));
+        }
+        return;
+    }
+    write_selection(sel_v, sel_i, K, t, idx_out, w_out);
+}
 
-    // weights: softmax over the K selected values
-    const float v0 = __shfl(sel_v, 0, WAVE);
-    const float ex = (l < K) ? expf(sel_v - v0) : 0.0f;
-    float sum = ex;
+// Re-decision of the queued tokens on exact logits, one block per token at a
+// time: the candidates are every expert whose estimate exceeds the cut (all E
+// if more than 64 do), their exact keys are computed four per wave pass, and
+// the first wave selects the top K among them.
+template <int VPL, typename XT>
+__global__ __launch_bounds__(256) void k_route_recheck(const float* __restrict__ est, int T, int E, int K,
+                                                       const int2* __restrict__ rc_list,
+                                                       const int32_t* __restrict__ rc_count,
+                                                       const XT* __restrict__ x, const float* __restrict__ wr,
+                                                       const float* __restrict__ bias, int H,
+                                                       int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+    __shared__ unsigned long long keys[VPL * WAVE];
+    __shared__ int cids[VPL * WAVE];
+    __shared__ int s_n;
+    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    const int n = rc_count[0];
+    for (int it = blockIdx.x; it < n; it += gridDim.x) {
+        const int2 ent = rc_list[it];
+        const int t = ent.x;
+        const float cut = __int_as_float(ent.y);
+        if (tid == 0) s_n = 0;
+        __syncthreads();
+        for (int e = tid; e < E; e += 256)
+            if (est[(long)t * E + e] > cut) cids[atomicAdd(&s_n, 1)] = e;
+        __syncthreads();
+        const bool all = s_n > SEL_CAP;
+        const int nc = all ? E : s_n;
+        const XT* xrow = x + (long)t * H;
+        for (int g = wave * 4; g < nc; g += 16) {
+            int ce[4];
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
-    if (l < K) {
-        idx_out[(long)t * K + l] = sel_i;
-        w_out[(long)t * K + l] = ex / sum;
+            for (int c = 0; c < 4; c++) ce[c] = g + c < nc ? (all ? g + c : cids[g + c]) : 0;
+            const int m = min(4, nc - g);
+            double d[4];
+            wave_dot_exact4(xrow, wr, ce, m, H, d);
+            if (l == 0) {
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    if (c < m) {
+                        float lv = (float)d[c];
+                        if (bias) lv = __fadd_rn(lv, bias[ce[c]]);
+                        keys[g + c] = route_key(lv, ce[c]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            unsigned long long k[VPL];
+#pragma unroll
+            for (int j = 0; j < VPL; j++) k[j] = l + j * WAVE < nc ? keys[l + j * WAVE] : 0ull;
+            const unsigned long long sel = select_rounds<VPL>(k, K);
+            write_selection(route_key_value(sel), route_key_index(sel), K, t, idx_out, w_out);
+        }
+        __syncthreads();
     }
 }
 
@@ -377,36 +603,59 @@ hipError_t launch_logits_exact(const void* x, int x_bf16, const float* wr, const
     return hipGetLastError();
 }
 
+bool logits_fast_eligible(int T, int H, int E) {
+    return H % LM_BK == 0 && E % 4 == 0 && (size_t)T * H * 2 < ((size_t)1 << 32) &&
+           (size_t)3 * E * H * 2 < ((size_t)1 << 32);
+}
+
+size_t logits_fast_planes_bytes(int H, int E) { return (size_t)3 * E * H * 2; }
+
 hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, hipStream_t st) {
-    dim3 grid((T + FL_BM - 1) / FL_BM, (E + FL_BN - 1) / FL_BN);
-    hipLaunchKernelGGL(k_logits_fast, grid, dim3(256), 0, st, x, wr, bias, T, H, E, logits);
+                              float* logits, uint16_t* planes, int32_t* rc_count, hipStream_t st) {
+    const long n4 = (long)E * H / 4;
+    hipLaunchKernelGGL(k_router_split, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, wr, n4, planes,
+                       (long)E * H, rc_count);
+    static bool attr = false;     // raising the dynamic LDS limit is per function, once
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_logits_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           2 * LM_STAGE);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int items = ((T + LM_BM - 1) / LM_BM) * ((E + LM_BN - 1) / LM_BN);
+    hipLaunchKernelGGL(k_logits_mfma, dim3((items + 7) / 8 * 8), dim3(256), 2 * LM_STAGE, st, x, planes, bias, T, H, E,
+                       logits);
     return hipGetLastError();
 }
 
 template <int VPL>
-static hipError_t sel_dispatch_x(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
-                                 int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                                 int32_t* nre, hipStream_t st) {
-    dim3 grid((T + 3) / 4);
+static hipError_t sel_dispatch(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
+                               int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
+                               int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st) {
+    hipLaunchKernelGGL((k_route_select<VPL>), dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K, tau, exact, idx, w,
+                       flags, rc_list, rc_count);
+    if (exact) return hipGetLastError();
+    const int grid = T < 256 ? T : 256;
     if (x_bf16)
-        hipLaunchKernelGGL((k_route_select<VPL, uint16_t>), grid, dim3(256), 0, st, logits, T, E, K, tau, exact,
-                           (const uint16_t*)x, wr, bias, H, idx, w, nre);
+        hipLaunchKernelGGL((k_route_recheck<VPL, uint16_t>), dim3(grid), dim3(256), 0, st, logits, T, E, K, rc_list,
+                           rc_count, (const uint16_t*)x, wr, bias, H, idx, w);
     else
-        hipLaunchKernelGGL((k_route_select<VPL, float>), grid, dim3(256), 0, st, logits, T, E, K, tau, exact,
-                           (const float*)x, wr, bias, H, idx, w, nre);
+        hipLaunchKernelGGL((k_route_recheck<VPL, float>), dim3(grid), dim3(256), 0, st, logits, T, E, K, rc_list,
+                           rc_count, (const float*)x, wr, bias, H, idx, w);
     return hipGetLastError();
 }
 
 hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
                                int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                               int32_t* rechecked, hipStream_t st) {
+                               int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st) {
     const int vpl = (E + WAVE - 1) / WAVE;
-    if (vpl <= 1) return sel_dispatch_x<1>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
-    if (vpl <= 2) return sel_dispatch_x<2>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
-    if (vpl <= 4) return sel_dispatch_x<4>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
-    if (vpl <= 8) return sel_dispatch_x<8>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
-    if (vpl <= 16) return sel_dispatch_x<16>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
-    if (vpl <= 32) return sel_dispatch_x<32>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
-    return sel_dispatch_x<64>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, rechecked, st);
+#define MOE_SEL(V) return sel_dispatch<V>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, flags, rc_list, rc_count, st)
+    if (vpl <= 1) MOE_SEL(1);
+    if (vpl <= 2) MOE_SEL(2);
+    if (vpl <= 4) MOE_SEL(4);
+    if (vpl <= 8) MOE_SEL(8);
+    if (vpl <= 16) MOE_SEL(16);
+    if (vpl <= 32) MOE_SEL(32);
+    MOE_SEL(64);
+#undef MOE_SEL
 }

@@ -175,6 +175,18 @@ def test_route_near_ties_are_rechecked():
     _route_case(x, wr, K, bias)
 
 
+def test_route_recheck_falls_back_to_all_experts():
+    # identical router rows: every estimate lies within the margin of the K-th,
+    # more than 64 candidates, so each token is re-decided on all E exact
+    # logits; the tiny distinct biases round to ties in places (lower id wins)
+    rng = np.random.default_rng(12)
+    T, H, E, K = 96, 256, 128, 4
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = np.tile((rng.standard_normal((1, H)) * 0.02).astype(np.float32), (E, 1))
+    bias = (np.arange(E, dtype=np.float32) * np.float32(3e-8)).astype(np.float32)
+    _route_case(x, wr, K, bias)
+
+
 def test_route_and_grouping_empty():
     wr = torch.zeros((8, 64), dtype=torch.float32, device="cuda")
     x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
