@@ -26,9 +26,6 @@
 //     sum_k x w = d (D - 136 S),  D = MFMA(x, 128 + u),  S = MFMA(x, 1)
 // so the row sums S come out of the same MFMA layout, and the weights enter
 // exactly (no rounding of d * q).
-#include <cstdio>
-#include <cstdlib>
-
 #include "common.h"
 #include "launch.h"
 
@@ -300,161 +297,6 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
     }
 }
 
-// ---------------------------------------------------------------------------- bf16: VALU dot products
-//
-// For bf16 weights the streaming pattern that HBM serves best is one
-// contiguous 1 KB chunk of a single weight row per wave instruction (64 lanes
-// x 16 B); the 16-row MFMA operand layout (16 rows x 64 B per instruction)
-// loses ~30% of the bandwidth at these sizes.  So here each lane multiplies its
-// 8 weights by the matching 8 activations of every token row with
-// v_dot2_f32_bf16, and the per-lane partial sums are combined across the wave
-// by a transposing butterfly: with V sums per lane, each xor step keeps half of
-// them and adds the partner's copy of that half, so after log2(V) steps lane l
-// holds the full sum of entry l >> (6 - log2 V) (remaining steps add copies).
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-MOE_DEV float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-MOE_DEV float dot8(uint4 w, uint4 x, float c) {
-    c = dot2(w.x, x.x, c);
-    c = dot2(w.y, x.y, c);
-    c = dot2(w.z, x.z, c);
-    return dot2(w.w, x.w, c);
-}
-
-// One butterfly step of the transposing reduction (CNT live entries, xor
-// distance D); fully unrolled at compile time so v[] stays in registers.
-template <int CNT, int D, int V>
-MOE_DEV void transpose_reduce_step(float (&v)[V], int l) {
-    if constexpr (D >= 1) {
-        if constexpr (CNT > 1) {
-            constexpr int half = CNT / 2;
-            const bool bit = (l & D) != 0;
-#pragma unroll
-            for (int i = 0; i < half; i++) {
-                const float keep = bit ? v[i + half] : v[i];
-                const float send = bit ? v[i] : v[i + half];
-                v[i] = keep + __shfl_xor(send, D, WAVE);
-            }
-            transpose_reduce_step<half, D / 2, V>(v, l);
-        } else {
-            v[0] += __shfl_xor(v[0], D, WAVE);
-            transpose_reduce_step<1, D / 2, V>(v, l);
-        }
-    }
-}
-
-// In-place transposing reduction of v[V] over the wave; returns the sum of
-// entry lane >> (6 - log2 V).
-template <int V>
-MOE_DEV float wave_transpose_reduce(float (&v)[V]) {
-    transpose_reduce_step<V, 32, V>(v, lane_id());
-    return v[0];
-}
-
-// gate/up: a wave owns FR feature rows (FR gate rows and the same FR up rows)
-// over the whole of H; WV waves per block share the expert's token rows in LDS.
-template <int NT, int CH, int FR, int WV>
-__global__ __launch_bounds__(64 * WV) void k_gateup_valu(const uint16_t* __restrict__ xp,
-                                                         const uint16_t* __restrict__ wg,
-                                                         const uint16_t* __restrict__ wu,
-                                                         const int4* __restrict__ list, int H, int F,
-                                                         uint16_t* __restrict__ abuf) {
-    const int4 ent = list[blockIdx.y];
-    const int e = ent.x, off = ent.y, n = ent.z;
-    if (e < 0) return;
-    const int wave = threadIdx.x / WAVE, l = lane_id();
-    const int f0 = (blockIdx.x * WV + wave) * FR;
-    // this wave's weight rows (gate f0.., up f0..), every 1 KB chunk in flight at once
-    const uint16_t* g0 = wg + ((long)e * F + f0) * H + l * 8;
-    const uint16_t* u0 = wu + ((long)e * F + f0) * H + l * 8;
-    uint4 w[2 * FR][CH];
-#pragma unroll
-    for (int c = 0; c < CH; c++) {
-#pragma unroll
-        for (int r = 0; r < FR; r++) {
-            w[r][c] = ld_nt(g0 + (long)r * H + c * 512);
-            w[FR + r][c] = ld_nt(u0 + (long)r * H + c * 512);
-        }
-    }
-    // the expert's token rows, once per block, into LDS
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    for (int i = threadIdx.x; i < n * (H / 8); i += blockDim.x)
-        *reinterpret_cast<uint4*>(xs + i * 8) = ld16(xp + (long)off * H + i * 8);
-    __syncthreads();
-    constexpr int V = 2 * FR * NT;
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; i++) acc[i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; c++) {
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-            uint4 a = make_uint4(0, 0, 0, 0);
-            if (t < n) a = *reinterpret_cast<const uint4*>(xs + t * H + c * 512 + l * 8);
-#pragma unroll
-            for (int r = 0; r < 2 * FR; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
-        }
-    }
-    // lane l now owns entry j = l >> shift: row r = j / NT (< FR: gate, else up), token t = j % NT
-    const float v = wave_transpose_reduce<V>(acc);
-    constexpr int shift = V == 8 ? 3 : V == 16 ? 2 : V == 32 ? 1 : 0;
-    const float up = __shfl_down(v, (FR * NT) << shift, WAVE);   // entry j + FR*NT: the matching up row
-    const int j = l >> shift;
-    const int r = j / NT, t = j % NT;
-    if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
-        abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_s(v) * up);
-}
-
-// down: a wave owns DR hidden rows over the whole of F; DW waves per block
-// share the expert's A rows in LDS.
-template <int NT, int YBF16, int FCH, int DR, int DW>
-__global__ __launch_bounds__(64 * DW) void k_down_valu(const uint16_t* __restrict__ abuf,
-                                                       const uint16_t* __restrict__ wd, const int4* __restrict__ list,
-                                                       int H, int F, void* __restrict__ y) {
-    const int4 ent = list[blockIdx.y];
-    const int e = ent.x, off = ent.y, n = ent.z;
-    if (e < 0) return;
-    const int wave = threadIdx.x / WAVE, l = lane_id();
-    const int h0 = (blockIdx.x * DW + wave) * DR;
-    uint4 w[DR][FCH];
-#pragma unroll
-    for (int c = 0; c < FCH; c++) {
-#pragma unroll
-        for (int r = 0; r < DR; r++) w[r][c] = ld_nt(wd + ((long)e * H + h0 + r) * F + c * 512 + l * 8);
-    }
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* as = reinterpret_cast<uint16_t*>(smem);
-    for (int i = threadIdx.x; i < n * (F / 8); i += blockDim.x)
-        *reinterpret_cast<uint4*>(as + i * 8) = ld16(abuf + (long)off * F + i * 8);
-    __syncthreads();
-    constexpr int V = DR * NT;
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; i++) acc[i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < FCH; c++) {
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-            uint4 a = make_uint4(0, 0, 0, 0);
-            if (t < n) a = *reinterpret_cast<const uint4*>(as + t * F + c * 512 + l * 8);
-#pragma unroll
-            for (int r = 0; r < DR; r++) acc[r * NT + t] = dot8(w[r][c], a, acc[r * NT + t]);
-        }
-    }
-    const float v = wave_transpose_reduce<V>(acc);
-    constexpr int shift = V == 8 ? 3 : V == 16 ? 2 : V == 32 ? 1 : 0;
-    const int j = l >> shift;
-    const int r = j / NT, t = j % NT;
-    if ((l & ((1 << shift) - 1)) == 0 && t < n) {
-        const long o = (long)(off + t) * H + h0 + r;
-        if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
-        else ((float*)y)[o] = v;
-    }
-}
-
 // ---------------------------------------------------------------------------- host
 
 static int ring_for(int steps) {
@@ -509,74 +351,13 @@ static void launch_wt(const uint16_t* xp, const void* wg, const void* wu, const 
     }
 }
 
-// Block shapes of the VALU kernels (feature rows per wave, waves per block;
-// hidden rows per wave, waves per block); MOE_SMALL_SHAPE="fr,wv,dr,dw" overrides them
-// for tuning runs.
-struct SmallShape { int fr = 2, wv = 4, dr = 8, dw = 4; };
-static SmallShape small_shape() {
-    static SmallShape sh = [] {
-        SmallShape v;
-        if (const char* e = getenv("MOE_SMALL_SHAPE")) sscanf(e, "%d,%d,%d,%d", &v.fr, &v.wv, &v.dr, &v.dw);
-        return v;
-    }();
-    return sh;
-}
-
-template <int NT, int CH, int FR, int WV>
-static void gu_valu(int slots, int H, int F, const uint16_t* xp, const void* wg, const void* wu, const int4* list,
-                    uint16_t* abuf, hipStream_t st) {
-    hipLaunchKernelGGL((k_gateup_valu<NT, CH, FR, WV>), dim3(F / (FR * WV), slots), dim3(64 * WV), (size_t)NT * H * 2,
-                       st, xp, (const uint16_t*)wg, (const uint16_t*)wu, list, H, F, abuf);
-}
-template <int NT, int YB, int FCH, int DR, int DW>
-static void dn_valu(int slots, int H, int F, const uint16_t* abuf, const void* wd, const int4* list, void* y,
-                    hipStream_t st) {
-    hipLaunchKernelGGL((k_down_valu<NT, YB, FCH, DR, DW>), dim3(H / (DR * DW), slots), dim3(64 * DW),
-                       (size_t)NT * F * 2, st, abuf, (const uint16_t*)wd, list, H, F, y);
-}
-template <int NT, int YB, int FCH>
-static void dn_valu_shape(const SmallShape& sh, int slots, int H, int F, const uint16_t* abuf, const void* wd,
-                          const int4* list, void* y, hipStream_t st) {
-    if (sh.dr == 4 && sh.dw == 4) dn_valu<NT, YB, FCH, 4, 4>(slots, H, F, abuf, wd, list, y, st);
-    else if (sh.dr == 4 && sh.dw == 8) dn_valu<NT, YB, FCH, 4, 8>(slots, H, F, abuf, wd, list, y, st);
-    else if (sh.dr == 8 && sh.dw == 8) dn_valu<NT, YB, FCH, 8, 8>(slots, H, F, abuf, wd, list, y, st);
-    else dn_valu<NT, YB, FCH, 8, 4>(slots, H, F, abuf, wd, list, y, st);
-}
-
-template <int NT, int CH, int FCH>
-static void launch_valu(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
-                        int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
-    const SmallShape sh = small_shape();
-    if (sh.fr == 1 && sh.wv == 4) gu_valu<NT, CH, 1, 4>(slots, H, F, xp, wg, wu, list, abuf, st);
-    else if (sh.fr == 1 && sh.wv == 8) gu_valu<NT, CH, 1, 8>(slots, H, F, xp, wg, wu, list, abuf, st);
-    else if (sh.fr == 2 && sh.wv == 8) gu_valu<NT, CH, 2, 8>(slots, H, F, xp, wg, wu, list, abuf, st);
-    else gu_valu<NT, CH, 2, 4>(slots, H, F, xp, wg, wu, list, abuf, st);
-    if (y_bf16) dn_valu_shape<NT, 1, FCH>(sh, slots, H, F, abuf, wd, list, y, st);
-    else dn_valu_shape<NT, 0, FCH>(sh, slots, H, F, abuf, wd, list, y, st);
-}
-
-template <int NT, int CH>
-static void launch_valu_f(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
-                          int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
-    if (F == 512) launch_valu<NT, CH, 1>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
-    else launch_valu<NT, CH, 2>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
-}
-
-template <int NT>
-static void launch_valu_h(const uint16_t* xp, const void* wg, const void* wu, const void* wd, const int4* list,
-                          int slots, int H, int F, void* y, int y_bf16, uint16_t* abuf, hipStream_t st) {
-    switch (H / 512) {
-        case 1: launch_valu_f<NT, 1>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
-        case 2: launch_valu_f<NT, 2>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
-        case 4: launch_valu_f<NT, 4>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
-        default: launch_valu_f<NT, 8>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st); break;
-    }
-}
-
 hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const void* wu, const void* wd,
                             const void* sg, const void* su, const void* sd, const int32_t* offsets,
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                             hipStream_t st) {
+    // bf16, T <= 8: the persistent streaming kernels (no preparation pass)
+    if (w_dtype == SDT_BF16 && ffn_stream_eligible(T, K, E, H, F))
+        return launch_ffn_stream(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
     const int n = T * K;
     const int slots = E < n ? E : n;          // at most this many experts are touched
     char* base = (char*)ws;
@@ -587,14 +368,6 @@ hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const vo
     const int prep_blocks = (int)((chunks + 255) / 256);
     hipLaunchKernelGGL(k_small_prep, dim3(prep_blocks > 0 ? prep_blocks : 1), dim3(256), 0, st, (const uint16_t*)x,
                        offsets, perm, K, H, E, n, slots, list, xp);
-    // bf16, T <= 8, whole 1 KB rows: contiguous-row VALU kernels
-    const int hc = H / 512;
-    if (w_dtype == SDT_BF16 && T <= 8 && H % 512 == 0 && (hc == 1 || hc == 2 || hc == 4 || hc == 8) &&
-        (F == 512 || F == 1024)) {
-        if (T <= 4) launch_valu_h<4>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
-        else launch_valu_h<8>(xp, wg, wu, wd, list, slots, H, F, y, y_bf16, abuf, st);
-        return hipGetLastError();
-    }
     if (w_dtype == SDT_BF16)
         launch_wt<SDT_BF16>(xp, wg, wu, wd, sg, su, sd, list, slots, H, F, y, y_bf16, abuf, st);
     else

@@ -1,0 +1,362 @@
+// ffn_stream.hip -- the expert FFN for a handful of tokens (T <= 8: the
+// speculative verify step of 4 drafts + 1, and decode), bf16 weights.
+//
+// Per touched expert e with rows p in [off_e, off_e + n_e) (token perm[p] / K):
+//   a[p] = bf16(silu(x Wg_e^T) * (x Wu_e^T)),   y_perm[p] = a[p] Wd_e^T
+// (expert = gate/up/down matrices, "Strata Coder 编程模型深度剖析" §3).
+//
+// At this size the layer is one stream of expert weights (each touched
+// expert's matrices are read once, ~1 flop per byte), so the kernels are built
+// to keep HBM busy:
+//   * persistent blocks (two per CU); every wave walks its own sequence of
+//     equal-sized work items (FR feature rows of gate and up, or DR hidden rows
+//     of down), consecutive items going to concurrently running waves so the
+//     weight rows in flight at any moment are contiguous;
+//   * the next item's weight rows are loaded (non-temporal 16-byte loads, one
+//     contiguous 1 KB chunk of a row per wave instruction, never predicated)
+//     while the current item is multiplied, so the loads of a wave never stop;
+//   * the operands that are reused, the token rows (gate/up) or all the
+//     intermediate rows (down), sit in LDS, loaded once per block, together
+//     with the touched-expert list, which every block derives from the
+//     grouping offsets itself (no preparation kernel);
+//   * each lane multiplies its 8 weights by the matching 8 activations of every
+//     row of the expert with v_dot2_f32_bf16; the per-lane partial sums are
+//     combined across the wave by a transposing butterfly (with V sums per
+//     lane, each xor step keeps half of them and adds the partner's copy of
+//     that half, so lane l ends with the full sum of entry l >> (6 - log2 V)).
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+MOE_DEV uint4 ldnt16(const void* p) {
+    const u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+MOE_DEV float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c, false);
+}
+MOE_DEV float dot8bf(uint4 w, uint4 x, float c) {
+    c = dot2bf(w.x, x.x, c);
+    c = dot2bf(w.y, x.y, c);
+    c = dot2bf(w.z, x.z, c);
+    return dot2bf(w.w, x.w, c);
+}
+MOE_DEV float silu_ref(float g) { return g / (1.0f + expf(-g)); }
+
+template <int CNT, int D, int V>
+MOE_DEV void tr_step(float (&v)[V], int l) {
+    if constexpr (D >= 1) {
+        if constexpr (CNT > 1) {
+            constexpr int half = CNT / 2;
+            const bool bit = (l & D) != 0;
+#pragma unroll
+            for (int i = 0; i < half; i++) {
+                const float keep = bit ? v[i + half] : v[i];
+                const float send = bit ? v[i] : v[i + half];
+                v[i] = keep + __shfl_xor(send, D, WAVE);
+            }
+            tr_step<half, D / 2, V>(v, l);
+        } else {
+            v[0] += __shfl_xor(v[0], D, WAVE);
+            tr_step<1, D / 2, V>(v, l);
+        }
+    }
+}
+// in-place transposing reduction of v[V] (V a power of two <= 64) over the
+// wave; returns the sum of entry lane >> (6 - log2 V)
+template <int V>
+MOE_DEV float wave_tr_reduce(float (&v)[V]) {
+    tr_step<V, 32, V>(v, lane_id());
+    return v[0];
+}
+template <int V>
+constexpr int tr_shift() { return V == 64 ? 0 : V == 32 ? 1 : V == 16 ? 2 : V == 8 ? 3 : V == 4 ? 4 : V == 2 ? 5 : 6; }
+
+// The touched experts (count > 0) in expert order as (expert, first row,
+// rows), built by the whole block from the grouping offsets; returns their
+// number.  Needs 256 threads and E <= 256 * EPT.
+constexpr int EPT = 16;
+MOE_DEV int block_touched_list(const int32_t* __restrict__ offsets, int E, int4* __restrict__ list, int* scan) {
+    const int tid = threadIdx.x;
+    int off[EPT + 1];
+    const int e0 = tid * EPT;
+#pragma unroll
+    for (int i = 0; i <= EPT; i++) off[i] = e0 + i <= E ? offsets[min(e0 + i, E)] : 0;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; i++) cnt += (e0 + i < E && off[i + 1] > off[i]) ? 1 : 0;
+    // block exclusive scan of cnt
+    const int incl = wave_incl_scan(cnt);
+    const int w = tid / WAVE;
+    if (lane_id() == WAVE - 1) scan[w] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; i++) base += scan[i];
+    const int total = scan[0] + scan[1] + scan[2] + scan[3];
+    int pos = base + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < EPT; i++)
+        if (e0 + i < E && off[i + 1] > off[i]) list[pos++] = make_int4(e0 + i, off[i], off[i + 1] - off[i], 0);
+    return total;
+}
+
+// Copy n_kb KB from global memory to the start of LDS with the LDS DMA, the
+// block's 4 waves taking alternate 1 KB pieces (64 lanes x 16 B each).
+typedef __attribute__((address_space(3))) void lds_void_s;
+MOE_DEV void stage_lds(const void* src, int n_kb, unsigned char* lds, int wave, int l) {
+    const unsigned char* g = (const unsigned char*)src + l * 16;
+    for (int i = wave; i < n_kb; i += 4)
+        __builtin_amdgcn_global_load_lds(g + (long)i * 1024, (lds_void_s*)(lds + i * 1024), 16, 0, 0);
+}
+
+// A wave's walk over items it, it + W, it + 2W, ... < n: RING weight buffers,
+// the load of the item RING-1 steps ahead is issued before each multiply, so
+// RING-1 items' weights are always in flight.  Loads past the end repeat the
+// last item (never predicated); all have landed when the walk returns.
+template <int RING, typename Buf, typename LoadF, typename ComputeF>
+MOE_DEV void ring_walk(int it, int W, int n, Buf (&buf)[RING], LoadF&& load, ComputeF&& compute) {
+#pragma unroll
+    for (int b = 0; b < RING - 1; b++) load(min(it + b * W, n - 1), buf[b]);
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int b = 0; b < RING; b++) {
+            if (more) {
+                load(min(it + (RING - 1) * W, n - 1), buf[(b + RING - 1) % RING]);
+                compute(it, buf[b]);
+                it += W;
+                more = it < n;
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the repeated tail loads land before the wave ends
+}
+
+}  // namespace
+
+// gate/up.  Item = (touched expert j, feature tile): FR gate rows and the same
+// FR up rows over the whole of H = CH x 512.  LDS: the T token rows, the
+// touched list, the token of every grouped row.
+template <int NT, int CH, int FR, int RING>
+__global__ __launch_bounds__(256) void k_gateup_stream(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
+                                                       const uint16_t* __restrict__ wu,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ perm, int T, int K, int E, int F,
+                                                       uint16_t* __restrict__ abuf) {
+    constexpr int H = CH * 512;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                          // [T][H]
+    int4* list = reinterpret_cast<int4*>(smem + (size_t)T * H * 2);            // [<= T*K]
+    int* prow = reinterpret_cast<int*>(list + T * K);                          // [T*K] token of grouped row
+    __shared__ int scan[4];
+    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    // the token rows go to LDS by DMA (1 KB per instruction), issued first so
+    // that they land with the offsets the touched list is built from
+    stage_lds(x, T * H * 2 / 1024, smem, wave, l);
+    for (int i = tid; i < T * K; i += 256) prow[i] = perm[i] / K;
+    const int nlist = block_touched_list(offsets, E, list, scan);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+
+    const int tpe = F / FR;                     // items per expert
+    const int n_items = nlist * tpe;
+    const int W = gridDim.x * 4;
+    int it = blockIdx.x * 4 + wave;
+    if (it >= n_items) return;
+
+    uint4 wbuf[RING][2 * FR][CH];
+    auto load = [&](int item, uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
+        const int e = list[item / tpe].x, f0 = (item % tpe) * FR;
+        const uint16_t* g0 = wg + ((long)e * F + f0) * H + l * 8;
+        const uint16_t* u0 = wu + ((long)e * F + f0) * H + l * 8;
+#pragma unroll
+        for (int c = 0; c < CH; c++)
+#pragma unroll
+            for (int r = 0; r < FR; r++) {
+                w[r][c] = ldnt16(g0 + (long)r * H + c * 512);
+                w[FR + r][c] = ldnt16(u0 + (long)r * H + c * 512);
+            }
+    };
+    auto compute = [&](int item, const uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
+        const int4 ent = list[item / tpe];
+        const int off = ent.y, n = ent.z, f0 = (item % tpe) * FR;
+        constexpr int V = 2 * FR * NT;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (t < n) {
+                const uint16_t* xr = xs + prow[off + t] * H + l * 8;
+#pragma unroll
+                for (int c = 0; c < CH; c++) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(xr + c * 512);
+#pragma unroll
+                    for (int r = 0; r < 2 * FR; r++) acc[r * NT + t] = dot8bf(w[r][c], a, acc[r * NT + t]);
+                }
+            }
+        }
+        // lane l owns entry j = l >> shift: row r = j / NT (< FR gate, else up), token t = j % NT
+        const float v = wave_tr_reduce<V>(acc);
+        constexpr int shift = tr_shift<V>();
+        const float up = __shfl_down(v, (FR * NT) << shift, WAVE);
+        const int j = l >> shift, r = j / NT, t = j % NT;
+        if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
+            abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+    };
+    ring_walk<RING>(it, W, n_items, wbuf, load, compute);
+}
+
+// down.  Item = (touched expert j, hidden tile): DR rows of Wd over the whole
+// of F = FCH x 512.  LDS: all T*K intermediate rows, the touched list.
+template <int NT, int FCH, int DR, int YBF16, int RING>
+__global__ __launch_bounds__(256) void k_down_stream(const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ wd,
+                                                     const int32_t* __restrict__ offsets, int nrows, int E, int H,
+                                                     void* __restrict__ y) {
+    constexpr int F = FCH * 512;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* as = reinterpret_cast<uint16_t*>(smem);                           // [nrows][F]
+    int4* list = reinterpret_cast<int4*>(smem + (size_t)nrows * F * 2);         // [<= nrows]
+    __shared__ int scan[4];
+    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    stage_lds(abuf, nrows * F * 2 / 1024, smem, wave, l);
+    const int nlist = block_touched_list(offsets, E, list, scan);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+
+    const int tpe = H / DR;
+    const int n_items = nlist * tpe;
+    const int W = gridDim.x * 4;
+    int it = blockIdx.x * 4 + wave;
+    if (it >= n_items) return;
+
+    uint4 wbuf[RING][DR][FCH];
+    auto load = [&](int item, uint4 (&w)[DR][FCH]) __attribute__((always_inline)) {
+        const int e = list[item / tpe].x, h0 = (item % tpe) * DR;
+        const uint16_t* d0 = wd + ((long)e * H + h0) * F + l * 8;
+#pragma unroll
+        for (int c = 0; c < FCH; c++)
+#pragma unroll
+            for (int r = 0; r < DR; r++) w[r][c] = ldnt16(d0 + (long)r * F + c * 512);
+    };
+    auto compute = [&](int item, const uint4 (&w)[DR][FCH]) __attribute__((always_inline)) {
+        const int4 ent = list[item / tpe];
+        const int off = ent.y, n = ent.z, h0 = (item % tpe) * DR;
+        constexpr int V = DR * NT;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (t < n) {
+                const uint16_t* ar = as + (off + t) * F + l * 8;
+#pragma unroll
+                for (int c = 0; c < FCH; c++) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(ar + c * 512);
+#pragma unroll
+                    for (int r = 0; r < DR; r++) acc[r * NT + t] = dot8bf(w[r][c], a, acc[r * NT + t]);
+                }
+            }
+        }
+        const float v = wave_tr_reduce<V>(acc);
+        constexpr int shift = tr_shift<V>();
+        const int j = l >> shift, r = j / NT, t = j % NT;
+        if ((l & ((1 << shift) - 1)) == 0 && t < n) {
+            const long o = (long)(off + t) * H + h0 + r;
+            if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
+            else ((float*)y)[o] = v;
+        }
+    };
+    ring_walk<RING>(it, W, n_items, wbuf, load, compute);
+}
+
+// ---------------------------------------------------------------------------- host
+
+namespace {
+constexpr int GU_FR = 2, DN_DR = 8;
+constexpr int GU_RING = 2, DN_RING = 2;      // weight buffers per wave (16 KB / 8 KB items)
+constexpr size_t STREAM_LDS_MAX = 64 * 1024;    // two blocks per CU
+
+size_t gu_lds(int T, int K, int H) { return (size_t)T * H * 2 + (size_t)T * K * 16 + (size_t)T * K * 4; }
+size_t dn_lds(int T, int K, int F) { return (size_t)T * K * F * 2 + (size_t)T * K * 16; }
+
+int stream_grid(hipError_t& err) {
+    int dev = 0, ncu = 0;
+    err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return 2 * (ncu > 0 ? ncu : 1);
+}
+
+template <typename KF>
+hipError_t set_lds(KF kern, size_t lds) {
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <int NT, int CH>
+hipError_t gu_launch(int grid, hipStream_t st, const uint16_t* x, const void* wg, const void* wu,
+                     const int32_t* offsets, const int32_t* perm, int T, int K, int E, int F, uint16_t* abuf) {
+    auto kern = k_gateup_stream<NT, CH, GU_FR, GU_RING>;
+    const size_t lds = gu_lds(T, K, CH * 512);
+    hipError_t e = set_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, x, (const uint16_t*)wg, (const uint16_t*)wu, offsets,
+                       perm, T, K, E, F, abuf);
+    return hipSuccess;
+}
+
+template <int NT, int FCH, int YB>
+hipError_t dn_launch(int grid, hipStream_t st, const uint16_t* abuf, const void* wd, const int32_t* offsets,
+                     int nrows, int T, int K, int E, int H, void* y) {
+    auto kern = k_down_stream<NT, FCH, DN_DR, YB, DN_RING>;
+    const size_t lds = dn_lds(T, K, FCH * 512);
+    hipError_t e = set_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, abuf, (const uint16_t*)wd, offsets, nrows, E, H, y);
+    return hipSuccess;
+}
+
+template <int NT>
+hipError_t stream_nt(int grid, hipStream_t st, const uint16_t* x, const void* wg, const void* wu, const void* wd,
+                     const int32_t* offsets, const int32_t* perm, int T, int K, int E, int H, int F, void* y,
+                     int y_bf16, uint16_t* abuf) {
+    hipError_t e;
+    switch (H / 512) {
+        case 1: e = gu_launch<NT, 1>(grid, st, x, wg, wu, offsets, perm, T, K, E, F, abuf); break;
+        case 2: e = gu_launch<NT, 2>(grid, st, x, wg, wu, offsets, perm, T, K, E, F, abuf); break;
+        case 4: e = gu_launch<NT, 4>(grid, st, x, wg, wu, offsets, perm, T, K, E, F, abuf); break;
+        default: e = gu_launch<NT, 8>(grid, st, x, wg, wu, offsets, perm, T, K, E, F, abuf); break;
+    }
+    if (e != hipSuccess) return e;
+    const int nrows = T * K;
+    if (F == 512)
+        return y_bf16 ? dn_launch<NT, 1, 1>(grid, st, abuf, wd, offsets, nrows, T, K, E, H, y)
+                      : dn_launch<NT, 1, 0>(grid, st, abuf, wd, offsets, nrows, T, K, E, H, y);
+    return y_bf16 ? dn_launch<NT, 2, 1>(grid, st, abuf, wd, offsets, nrows, T, K, E, H, y)
+                  : dn_launch<NT, 2, 0>(grid, st, abuf, wd, offsets, nrows, T, K, E, H, y);
+}
+}  // namespace
+
+bool ffn_stream_eligible(int T, int K, int E, int H, int F) {
+    const int hc = H / 512;
+    return T >= 1 && T <= 8 && H % 512 == 0 && (hc == 1 || hc == 2 || hc == 4 || hc == 8) && (F == 512 || F == 1024) &&
+           E <= 256 * EPT && gu_lds(T, K, H) <= STREAM_LDS_MAX && dn_lds(T, K, F) <= STREAM_LDS_MAX;
+}
+
+size_t ffn_stream_workspace_bytes(int T, int K, int F) { return ((size_t)T * K * F * 2 + 255) / 256 * 256; }
+
+hipError_t launch_ffn_stream(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
+                             hipStream_t st) {
+    hipError_t err;
+    const int grid = stream_grid(err);
+    if (err != hipSuccess) return err;
+    uint16_t* abuf = (uint16_t*)ws;
+    err = T <= 4 ? stream_nt<4>(grid, st, (const uint16_t*)x, wg, wu, wd, offsets, perm, T, K, E, H, F, y, y_bf16, abuf)
+                 : stream_nt<8>(grid, st, (const uint16_t*)x, wg, wu, wd, offsets, perm, T, K, E, H, F, y, y_bf16, abuf);
+    if (err != hipSuccess) return err;
+    return hipGetLastError();
+}

@@ -38,6 +38,13 @@ hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const vo
                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                             hipStream_t st);
 
+// ffn_stream.hip (bf16, T <= 8; uses the first T*K*F*2 bytes of the small-path workspace)
+bool ffn_stream_eligible(int T, int K, int E, int H, int F);
+size_t ffn_stream_workspace_bytes(int T, int K, int F);
+hipError_t launch_ffn_stream(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                             const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
+                             hipStream_t st);
+
 // ffn_gemm.hip (many rows per expert; bf16 weights)
 bool ffn_gemm_eligible(int T, int K, int H, int F);
 size_t ffn_gemm_workspace_bytes(int T, int K, int E, int H, int F);
