@@ -94,6 +94,52 @@ MOE_DEV unsigned long long wave_max_u64(unsigned long long k) {
     return k;
 }
 
+// Wave-wide maximum of a u32, returned wave-uniform: DPP within each row of
+// 16 lanes (quad swaps, half-row and row mirrors), then the four row maxima.
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+MOE_DEV float order_key_value(uint32_t h) { return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h); }
+
+// Top-`rounds` under (value desc, expert asc) of the order keys kv[j] of expert
+// e = lane + 64 j (0 = absent; every finite or infinite logit has a key > 0):
+// lane r < rounds receives round r's key and expert.  Per round: the lane
+// maxima, their wave maximum M, and the lowest expert holding M (lowest j,
+// then lowest lane, by ballot), which is then cleared.
+template <int VPL>
+MOE_DEV void select_top(uint32_t (&kv)[VPL], int rounds, uint32_t& my_key, int& my_e) {
+    const int l = lane_id();
+    my_key = 0;
+    my_e = 0;
+    for (int r = 0; r < rounds; r++) {
+        uint32_t m = kv[0];
+#pragma unroll
+        for (int j = 1; j < VPL; j++) m = max(m, kv[j]);
+        const uint32_t M = wave_max_u32(m);
+        int win = -1;
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            if (win < 0) {
+                const unsigned long long bm = __ballot(kv[j] == M);
+                if (bm) win = (__ffsll((long long)bm) - 1) + j * WAVE;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; j++) kv[j] = (l + j * WAVE == win) ? 0u : kv[j];
+        if (l == r) {
+            my_key = M;
+            my_e = win;
+        }
+    }
+}
+
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // The tile that block `bid` of a grouped launch works on: experts own

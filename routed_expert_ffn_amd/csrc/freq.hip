@@ -8,14 +8,20 @@
 // "专家配置文件：48 x 256 的全量排名").
 //
 //   k_freq_count  top-K of every logit row (routing's rule: larger first, ties
-//                 to the lower id), per-block LDS histogram, int64 totals via
-//                 integer atomics (exact and order-independent).
+//                 to the lower id; the same wave selection as routing's),
+//                 per-block LDS histogram, int64 totals via integer atomics
+//                 (exact and order-independent).
 //   k_freq_rank   per layer: rank_of[e] = number of experts ahead of e in
 //                 (count desc, id asc) order; keep_map = ids of rank < keep in
 //                 ascending id order.
 #include "common.h"
 #include "launch.h"
 
+// One wave per logit row, rows walked with a stride so every block sees many;
+// the next row's logits are loaded while the current one is selected.  The
+// selection is routing's (select_top: order keys, ties to the lower id); each
+// of the K winners adds one to its expert's LDS bin, and the block's bins go
+// to the int64 totals with one atomic per expert at the end.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ logits, int64_t T, int E, int K,
                                                     int64_t rows_per_layer_blocks, unsigned long long* __restrict__ counts) {
@@ -25,31 +31,30 @@ __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ lo
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     __syncthreads();
     const int wave = threadIdx.x / WAVE, l = lane_id();
-    const float NEG = -__builtin_inff();
     const float* base = logits + (long)layer * T * E;
-    for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < T; t += rows_per_layer_blocks * 4) {
-        const float* row = base + t * E;
-        float v[VPL];
+    const int64_t step = rows_per_layer_blocks * 4;
+    int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    float cur[VPL], nxt[VPL];
+    auto load = [&](int64_t row, float (&v)[VPL]) __attribute__((always_inline)) {
+        const float* r = base + (row < T ? row : T - 1) * E;   // past the end: re-read the last row (unused)
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
             const int e = l + j * WAVE;
-            v[j] = e < E ? row[e] : NEG;
+            v[j] = __builtin_nontemporal_load(r + (e < E ? e : E - 1));
         }
-        unsigned long long taken = 0;
-        for (int r = 0; r < K; r++) {
-            float bv = NEG;
-            int bi = 0x7FFFFFFF;
+    };
+    if (t < T) load(t, cur);
+    for (; t < T; t += step) {
+        load(t + step, nxt);
+        uint32_t kv[VPL];
 #pragma unroll
-            for (int j = 0; j < VPL; j++) {
-                const int e = l + j * WAVE;
-                if (e < E && !((taken >> j) & 1ull) && key_better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
-            }
-            wave_best(bv, bi);
-            if ((bi & (WAVE - 1)) == l) {
-                taken |= 1ull << (bi / WAVE);
-                atomicAdd(&hist[bi], 1);
-            }
-        }
+        for (int j = 0; j < VPL; j++) kv[j] = l + j * WAVE < E ? f32_order_key(cur[j]) : 0u;
+        uint32_t key;
+        int e;
+        select_top<VPL>(kv, K, key, e);
+        if (l < K && e >= 0) atomicAdd(&hist[e], 1);   // e < 0 only if keys ran out (NaN rows)
+#pragma unroll
+        for (int j = 0; j < VPL; j++) cur[j] = nxt[j];
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x)
