@@ -11,7 +11,7 @@ Further workloads (the 8192-token prefill chunk, the pruning statistic over
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workloads verify,prefill,freq,stack]
+    python bench.py [--steps K] [--warmup W] [--workloads verify,prefill,freq,stack,copy]
 """
 from __future__ import annotations
 
@@ -43,9 +43,20 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, src_sha):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+# kernel sources behind each measured entry point (the counter summary is void
+# once any of them changes)
+SRC = {
+    "ffn_verify": ("ffn_stream.hip", "ffn_small.hip", "ffn.hip", "common.h"),
+    "ffn_prefill": ("ffn_gemm.hip", "ffn.hip", "common.h"),
+    "freq": ("freq.hip", "common.h"),
+}
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE of the entry point's kernels, each scaled by the
+    same counter's reading on a plain copy of known size), if it was taken on
+    the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -53,7 +64,7 @@ def measured_traffic(kernel_key, src_sha):
         d = json.load(open(p)).get(kernel_key)
     except (OSError, ValueError):
         return None
-    if not d or d.get("src_sha") != src_sha:
+    if not d or d.get("src_sha") != src_hash(*SRC[kernel_key]):
         return None
     return d.get("bytes_per_launch")
 
@@ -194,16 +205,16 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
     return res
 
 
-def roofline_for(res, bound, kernel_key, src_sha):
+def roofline_for(res, bound, kernel_key):
     t = res["parts_us"]["ffn"] / 1e6
     if bound == "hbm":
         a = res["bytes_ffn"] / t / 1e9
         return dict(bound="hbm", achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(a / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic(kernel_key, src_sha), kernel="moe_ffn (gate/up + down launches)",
+                    traffic=measured_traffic(kernel_key), kernel="moe_ffn (gate/up + down launches)",
                     algorithmic_bytes_per_launch=int(res["bytes_ffn"]), launch_us=round(res["parts_us"]["ffn"], 2))
     a = res["flops_ffn"] / t / 1e12
     return dict(bound="mfma", achieved=round(a, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=round(a / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic(kernel_key, src_sha),
+                frac=round(a / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic(kernel_key),
                 kernel="moe_ffn (gate/up + down launches)", algorithmic_flops_per_launch=res["flops_ffn"],
                 launch_us=round(res["parts_us"]["ffn"], 2))
 
@@ -236,9 +247,27 @@ def bench_freq(torch, moe, synth, steps, warmup, use_graph):
                value=L * T / (ms / 1e3), unit="logit rows/s", steps=n, wall_s=wall,
                roofline=dict(bound="hbm", achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=round(a / HBM_PEAK_GBS, 4), kernel="moe_expert_freq",
-                             traffic=measured_traffic("freq", src_hash("freq.hip"))))
+                             traffic=measured_traffic("freq")))
     del lg
     return res
+
+
+# ------------------------------------------------------------------ copy (counter calibration)
+def bench_copy(torch, steps):
+    """A plain 1 GiB device-to-device copy: the reference reading of the HBM
+    byte counters (1 GiB fetched and 1 GiB written per launch)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    timer = Timer(torch)
+    timer.run(lambda: b.copy_(a), 2)
+    reps = max(3, steps // 20)
+    dt, wall = timer.run(lambda: b.copy_(a), reps)
+    ms = dt / reps * 1e3
+    del a, b
+    return dict(name="device copy 1 GiB (counter calibration)", ms_per_step=ms, steps=reps, wall_s=wall,
+                value=round(2 * n / (ms / 1e3) / 1e9, 1), unit="GB/s (read + write)", bytes_read=n, bytes_written=n)
 
 
 # ------------------------------------------------------------------ pruned 48-layer int4 stack
@@ -320,7 +349,7 @@ def main():
     if "prefill" in wl:
         r = bench_layer(torch, moe, synth, synth.PREFILL_BF16, 3, max(8, args.steps // 10), 8, 1, use_graph,
                         "prefill chunk 8192 tok, E512 top-10 bf16, Zipf(1.1) router offset")
-        r["roofline"] = roofline_for(r, "mfma", "ffn_prefill", src_hash("ffn.hip"))
+        r["roofline"] = roofline_for(r, "mfma", "ffn_prefill")
         r["unit"] = "tokens/s"
         log(f"[prefill] {r['ms_per_step']:.3f} ms/step  parts {r['parts_us']}")
         also.append(r)
@@ -328,6 +357,11 @@ def main():
     if "freq" in wl:
         r = bench_freq(torch, moe, synth, max(5, args.steps // 20), 2, use_graph)
         log(f"[freq] {r['ms_per_step']:.3f} ms/step")
+        also.append(r)
+        torch.cuda.empty_cache()
+    if "copy" in wl:
+        r = bench_copy(torch, args.steps)
+        log(f"[copy] {r['ms_per_step']:.3f} ms per 1 GiB copy, {r['value']} GB/s")
         also.append(r)
         torch.cuda.empty_cache()
     if "stack" in wl:
@@ -361,7 +395,7 @@ def main():
         "config": {"workload": main_res["name"], "tokens": main_res.get("T"), "hidden": 2048, "experts": 512,
                    "top_k": 10, "expert_width": 512, "weight_sets_rotated": N_SETS if "verify" in main_res["name"] else 1,
                    "hip_graph": use_graph},
-        "roofline": roofline_for(main_res, "hbm", "ffn_verify", src_hash("ffn.hip")) if "verify" in main_res["name"]
+        "roofline": roofline_for(main_res, "hbm", "ffn_verify") if "verify" in main_res["name"]
         else main_res.get("roofline"),
         "cpu_baseline": cpu,
         "step_breakdown_us": {k: round(v, 2) for k, v in main_res.get("parts_us", {}).items()},
