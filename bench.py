@@ -345,6 +345,7 @@ def main():
     if "verify" in wl:
         main_res = bench_layer(torch, moe, synth, synth.VERIFY_BF16, 2, args.steps, args.warmup, N_SETS, use_graph,
                                "verify step 5 tok, E512 top-10 bf16")
+        main_res["is_verify_layer"] = True
         log(f"[verify] {main_res['ms_per_step']*1e3:.1f} us/step  parts {main_res['parts_us']}")
     if "prefill" in wl:
         r = bench_layer(torch, moe, synth, synth.PREFILL_BF16, 3, max(8, args.steps // 10), 8, 1, use_graph,
@@ -377,7 +378,8 @@ def main():
         if main_res is None:
             sys.exit("no workload ran")
     cpu = None
-    if not args.no_cpu_baseline and main_res.get("T") == 5 and "verify" in main_res["name"]:
+    is_verify = main_res.get("is_verify_layer", False)
+    if not args.no_cpu_baseline and is_verify:
         cpu = cpu_baseline_verify(torch, synth)
     line = {
         "metric": METRIC,
@@ -393,9 +395,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": main_res["name"], "tokens": main_res.get("T"), "hidden": 2048, "experts": 512,
-                   "top_k": 10, "expert_width": 512, "weight_sets_rotated": N_SETS if "verify" in main_res["name"] else 1,
+                   "top_k": 10, "expert_width": 512, "weight_sets_rotated": N_SETS if is_verify else 1,
                    "hip_graph": use_graph},
-        "roofline": roofline_for(main_res, "hbm", "ffn_verify") if "verify" in main_res["name"]
+        "roofline": roofline_for(main_res, "hbm", "ffn_verify") if is_verify
         else main_res.get("roofline"),
         "cpu_baseline": cpu,
         "step_breakdown_us": {k: round(v, 2) for k, v in main_res.get("parts_us", {}).items()},

@@ -358,6 +358,8 @@ hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const vo
     // bf16, T <= 8: the persistent streaming kernels (no preparation pass)
     if (w_dtype == SDT_BF16 && ffn_stream_eligible(T, K, E, H, F))
         return launch_ffn_stream(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
+    if (w_dtype == SDT_INT4 && ffn_stream_q4_eligible(T, K, E, H, F))
+        return launch_ffn_stream_q4(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
     const int n = T * K;
     const int slots = E < n ? E : n;          // at most this many experts are touched
     char* base = (char*)ws;

@@ -274,6 +274,207 @@ __global__ __launch_bounds__(256) void k_down_stream(const uint16_t* __restrict_
     ring_walk<RING>(it, W, n_items, wbuf, load, compute);
 }
 
+// ---------------------------------------------------------------------------- int4 weights
+//
+// Block int4 (32 consecutive inputs share an fp16 scale d; value d (u - 8), u
+// the stored nibble, element 2j in the low nibble of byte j).  One lane's 16
+// bytes are exactly one quant block, so a 1 KB wave instruction reads 64
+// whole blocks.  The nibbles become the exact bf16 values 128 + u (bit pattern
+// 0x4300 | u), so with the block's activation sum S = sum x:
+//     sum_k x w = d (D - 136 S),  D = sum_k x (128 + u)   (v_dot2_f32_bf16)
+// and S comes from LDS, summed once per block of activations.
+
+namespace {
+// 8 nibbles -> 8 bf16 values 128 + u (dword i holds elements 2i, 2i+1)
+MOE_DEV uint4 nib8_bf16(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
+    o.y = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
+    o.z = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
+    o.w = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+    return o;
+}
+// D = sum over one 32-element block of x * (128 + u)
+MOE_DEV float dot_block_q4(uint4 q, const uint16_t* __restrict__ xl) {
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) d = dot8bf(nib8_bf16(w4[k]), *reinterpret_cast<const uint4*>(xl + k * 8), d);
+    return d;
+}
+MOE_DEV uint16_t ldnt_u16(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
+// sums of every 32-element block of `rows` LDS rows of `cols` bf16 into sums[row][cols/32]
+MOE_DEV void block_sums(const uint16_t* __restrict__ rowsp, int rows, int cols, float* __restrict__ sums) {
+    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+    const int nb = cols / 32;
+    for (int i = threadIdx.x; i < rows * nb; i += blockDim.x) {
+        const uint16_t* p = rowsp + (i / nb) * cols + (i % nb) * 32;
+        float sacc = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) sacc = dot8bf(ones, *reinterpret_cast<const uint4*>(p + k * 8), sacc);
+        sums[i] = sacc;
+    }
+}
+
+// transposing reduction within each 16-lane group (xor 8, 4, 2, 1): lane l
+// returns the group's full sum of entry (l & 15) >> (4 - log2 V)
+template <int V>
+MOE_DEV float group16_tr_reduce(float (&v)[V]) {
+    tr_step<V, 8, V>(v, lane_id());
+    return v[0];
+}
+}  // namespace
+
+// gate/up, int4.  Item = FR gate rows and the same FR up rows over all of
+// H = CH x 2048 (a lane: one quant block per row and chunk).
+template <int NT, int CH, int FR, int RING>
+__global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg,
+                                                          const uint8_t* __restrict__ wu, const uint16_t* __restrict__ sg,
+                                                          const uint16_t* __restrict__ su,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ perm, int T, int K, int E, int F,
+                                                          uint16_t* __restrict__ abuf) {
+    constexpr int H = CH * 2048;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                           // [T][H]
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)T * H * 2);           // [T][H/32]
+    int4* list = reinterpret_cast<int4*>(xsum + T * (H / 32));                  // [<= T*K]
+    int* prow = reinterpret_cast<int*>(list + T * K);                           // [T*K]
+    __shared__ int scan[4];
+    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    stage_lds(x, T * H * 2 / 1024, smem, wave, l);
+    for (int i = tid; i < T * K; i += 256) prow[i] = perm[i] / K;
+    const int nlist = block_touched_list(offsets, E, list, scan);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+    block_sums(xs, T, H, xsum);
+    __syncthreads();
+
+    const int tpe = F / FR;
+    const int n_items = nlist * tpe;
+    const int W = gridDim.x * 4;
+    const int it = blockIdx.x * 4 + wave;
+    if (it >= n_items) return;
+
+    struct Buf { uint4 q[2 * FR][CH]; uint16_t d[2 * FR][CH]; };
+    Buf wbuf[RING];
+    auto load = [&](int item, Buf& b) __attribute__((always_inline)) {
+        const long row0 = (long)list[item / tpe].x * F + (item % tpe) * FR;
+#pragma unroll
+        for (int r = 0; r < FR; r++)
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                b.q[r][c] = ldnt16(wg + (row0 + r) * (H / 2) + c * 1024 + l * 16);
+                b.q[FR + r][c] = ldnt16(wu + (row0 + r) * (H / 2) + c * 1024 + l * 16);
+                b.d[r][c] = ldnt_u16(sg + (row0 + r) * (H / 32) + c * 64 + l);
+                b.d[FR + r][c] = ldnt_u16(su + (row0 + r) * (H / 32) + c * 64 + l);
+            }
+    };
+    auto compute = [&](int item, const Buf& b) __attribute__((always_inline)) {
+        const int4 ent = list[item / tpe];
+        const int off = ent.y, n = ent.z, f0 = (item % tpe) * FR;
+        constexpr int V = 2 * FR * NT;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (t < n) {
+                const int tok = prow[off + t];
+#pragma unroll
+                for (int c = 0; c < CH; c++) {
+                    const uint16_t* xl = xs + tok * H + c * 2048 + l * 32;
+                    const float S = xsum[tok * (H / 32) + c * 64 + l];
+#pragma unroll
+                    for (int r = 0; r < 2 * FR; r++) {
+                        const float D = dot_block_q4(b.q[r][c], xl);
+                        acc[r * NT + t] = fmaf(fp16_to_f32(b.d[r][c]), fmaf(-136.0f, S, D), acc[r * NT + t]);
+                    }
+                }
+            }
+        }
+        const float v = wave_tr_reduce<V>(acc);
+        constexpr int shift = tr_shift<V>();
+        const float up = __shfl_down(v, (FR * NT) << shift, WAVE);
+        const int j = l >> shift, r = j / NT, t = j % NT;
+        if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
+            abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+    };
+    ring_walk<RING>(it, W, n_items, wbuf, load, compute);
+}
+
+// down, int4, F = 512: a 1 KB instruction covers 4 rows of Wd (16 lanes x one
+// quant block each).  Item = I instructions = 4I hidden rows.
+template <int NT, int I, int YBF16, int RING>
+__global__ __launch_bounds__(256) void k_down_stream_q4(const uint16_t* __restrict__ abuf, const uint8_t* __restrict__ wd,
+                                                        const uint16_t* __restrict__ sd,
+                                                        const int32_t* __restrict__ offsets, int nrows, int E, int H,
+                                                        void* __restrict__ y) {
+    constexpr int F = 512, NB = F / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t* as = reinterpret_cast<uint16_t*>(smem);                            // [nrows][F]
+    float* asum = reinterpret_cast<float*>(smem + (size_t)nrows * F * 2);        // [nrows][F/32]
+    int4* list = reinterpret_cast<int4*>(asum + nrows * NB);                     // [<= nrows]
+    __shared__ int scan[4];
+    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    stage_lds(abuf, nrows * F * 2 / 1024, smem, wave, l);
+    const int nlist = block_touched_list(offsets, E, list, scan);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    block_sums(as, nrows, F, asum);
+    __syncthreads();
+
+    const int tpe = H / (4 * I);
+    const int n_items = nlist * tpe;
+    const int W = gridDim.x * 4;
+    const int it = blockIdx.x * 4 + wave;
+    if (it >= n_items) return;
+    const int g = l >> 4, b = l & 15;            // row within an instruction, quant block within the row
+
+    struct Buf { uint4 q[I]; uint16_t d[I]; };
+    Buf wbuf[RING];
+    auto load = [&](int item, Buf& bf) __attribute__((always_inline)) {
+        const long row0 = (long)list[item / tpe].x * H + (item % tpe) * (4 * I) + g;
+#pragma unroll
+        for (int i = 0; i < I; i++) {
+            bf.q[i] = ldnt16(wd + (row0 + 4 * i) * (F / 2) + b * 16);
+            bf.d[i] = ldnt_u16(sd + (row0 + 4 * i) * NB + b);
+        }
+    };
+    auto compute = [&](int item, const Buf& bf) __attribute__((always_inline)) {
+        const int4 ent = list[item / tpe];
+        const int off = ent.y, n = ent.z, h0 = (item % tpe) * (4 * I);
+        constexpr int V = I * NT;
+        static_assert(V <= 16, "one entry per lane after the 16-lane reduction");
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (t < n) {
+                const uint16_t* al = as + (off + t) * F + b * 32;
+                const float S = asum[(off + t) * NB + b];
+#pragma unroll
+                for (int i = 0; i < I; i++) {
+                    const float D = dot_block_q4(bf.q[i], al);
+                    acc[i * NT + t] = fmaf(fp16_to_f32(bf.d[i]), fmaf(-136.0f, S, D), acc[i * NT + t]);
+                }
+            }
+        }
+        const float v = group16_tr_reduce<V>(acc);
+        constexpr int shift = V == 16 ? 0 : V == 8 ? 1 : V == 4 ? 2 : V == 2 ? 3 : 4;
+        const int j = b >> shift, i = j / NT, t = j % NT;
+        if ((b & ((1 << shift) - 1)) == 0 && t < n) {
+            const long o = (long)(off + t) * H + h0 + 4 * i + g;
+            if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
+            else ((float*)y)[o] = v;
+        }
+    };
+    ring_walk<RING>(it, W, n_items, wbuf, load, compute);
+}
+
 // ---------------------------------------------------------------------------- host
 
 namespace {
@@ -339,6 +540,65 @@ hipError_t stream_nt(int grid, hipStream_t st, const uint16_t* x, const void* wg
                   : dn_launch<NT, 2, 0>(grid, st, abuf, wd, offsets, nrows, T, K, E, H, y);
 }
 }  // namespace
+
+namespace {
+constexpr int Q4_FR = 4, Q4_I = 2, Q4_RING = 2;
+size_t gu_lds_q4(int T, int K, int H) { return (size_t)T * H * 2 + (size_t)T * (H / 32) * 4 + (size_t)T * K * 20; }
+size_t dn_lds_q4(int T, int K) { return (size_t)T * K * 512 * 2 + (size_t)T * K * 16 * 4 + (size_t)T * K * 16; }
+
+template <int NT, int CH>
+hipError_t gu_launch_q4(int grid, hipStream_t st, const uint16_t* x, const void* wg, const void* wu, const void* sg,
+                        const void* su, const int32_t* offsets, const int32_t* perm, int T, int K, int E, int F,
+                        uint16_t* abuf) {
+    auto kern = k_gateup_stream_q4<NT, CH, Q4_FR, Q4_RING>;
+    const size_t lds = gu_lds_q4(T, K, CH * 2048);
+    hipError_t e = set_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, x, (const uint8_t*)wg, (const uint8_t*)wu,
+                       (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, T, K, E, F, abuf);
+    return hipSuccess;
+}
+template <int NT, int YB>
+hipError_t dn_launch_q4(int grid, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd,
+                        const int32_t* offsets, int T, int K, int E, int H, void* y) {
+    auto kern = k_down_stream_q4<NT, Q4_I, YB, Q4_RING>;
+    const size_t lds = dn_lds_q4(T, K);
+    hipError_t e = set_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, abuf, (const uint8_t*)wd, (const uint16_t*)sd, offsets,
+                       T * K, E, H, y);
+    return hipSuccess;
+}
+template <int NT>
+hipError_t stream_q4_nt(int grid, hipStream_t st, const uint16_t* x, const void* wg, const void* wu, const void* wd,
+                        const void* sg, const void* su, const void* sd, const int32_t* offsets, const int32_t* perm,
+                        int T, int K, int E, int H, int F, void* y, int y_bf16, uint16_t* abuf) {
+    hipError_t e = gu_launch_q4<NT, 1>(grid, st, x, wg, wu, sg, su, offsets, perm, T, K, E, F, abuf);   // H = 2048
+    if (e != hipSuccess) return e;
+    return y_bf16 ? dn_launch_q4<NT, 1>(grid, st, abuf, wd, sd, offsets, T, K, E, H, y)
+                  : dn_launch_q4<NT, 0>(grid, st, abuf, wd, sd, offsets, T, K, E, H, y);
+}
+}  // namespace
+
+bool ffn_stream_q4_eligible(int T, int K, int E, int H, int F) {
+    return T >= 1 && T <= 8 && H == 2048 && F == 512 && E <= 256 * EPT &&
+           gu_lds_q4(T, K, H) <= STREAM_LDS_MAX && dn_lds_q4(T, K) <= STREAM_LDS_MAX;
+}
+
+hipError_t launch_ffn_stream_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
+                                const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
+                                int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st) {
+    hipError_t err;
+    const int grid = stream_grid(err);
+    if (err != hipSuccess) return err;
+    uint16_t* abuf = (uint16_t*)ws;
+    err = T <= 4 ? stream_q4_nt<4>(grid, st, (const uint16_t*)x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y,
+                                   y_bf16, abuf)
+                 : stream_q4_nt<8>(grid, st, (const uint16_t*)x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y,
+                                   y_bf16, abuf);
+    if (err != hipSuccess) return err;
+    return hipGetLastError();
+}
 
 bool ffn_stream_eligible(int T, int K, int E, int H, int F) {
     const int hc = H / 512;

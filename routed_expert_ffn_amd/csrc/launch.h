@@ -41,6 +41,10 @@ hipError_t launch_ffn_small(const void* x, int w_dtype, const void* wg, const vo
 // ffn_stream.hip (bf16, T <= 8; uses the first T*K*F*2 bytes of the small-path workspace)
 bool ffn_stream_eligible(int T, int K, int E, int H, int F);
 size_t ffn_stream_workspace_bytes(int T, int K, int F);
+bool ffn_stream_q4_eligible(int T, int K, int E, int H, int F);
+hipError_t launch_ffn_stream_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
+                                const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
+                                int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st);
 hipError_t launch_ffn_stream(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
                              const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                              hipStream_t st);

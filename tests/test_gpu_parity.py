@@ -83,7 +83,10 @@ SMALL = [
     synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="int4", zipf=True),
     synth.LayerShape(T=3, H=512, E=24, K=8, F=192, act="bf16", wdt="int4"),
     synth.LayerShape(T=1, H=768, E=300, K=10, F=64, act="bf16", wdt="bf16"),
-    # bf16, T <= 8, whole 1 KB rows: the contiguous-row VALU path
+    # int4, T <= 8, H 2048, F 512: the streaming int4 path (one quant block per lane)
+    synth.LayerShape(T=3, H=2048, E=24, K=8, F=512, act="bf16", wdt="int4"),
+    synth.LayerShape(T=8, H=2048, E=6, K=4, F=512, act="bf16", wdt="int4", zipf=True),
+    # bf16, T <= 8, whole 1 KB rows: the streaming bf16 path
     synth.LayerShape(T=7, H=1024, E=40, K=6, F=512, act="bf16", wdt="bf16", zipf=True),
     synth.LayerShape(T=3, H=512, E=16, K=4, F=1024, act="bf16", wdt="bf16"),
 ]
