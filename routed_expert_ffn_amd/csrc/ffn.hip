@@ -335,7 +335,6 @@ __global__ __launch_bounds__(256) void k_down_f32(const float* __restrict__ abuf
 // ---- host ------------------------------------------------------------------------
 
 size_t ffn_workspace_bytes(int T, int K, int E, int H, int F, int x_dtype, int w_dtype) {
-    (void)w_dtype;
     const size_t n = (size_t)T * K;
     const size_t elt = x_dtype == DT_F32 ? 4 : 2;
     size_t b = ((n * F * elt) + 255) / 256 * 256;
@@ -345,6 +344,10 @@ size_t ffn_workspace_bytes(int T, int K, int E, int H, int F, int x_dtype, int w
     }
     if (x_dtype != DT_F32 && ffn_gemm_eligible(T, K, H, F)) {
         const size_t s = ffn_gemm_workspace_bytes(T, K, E, H, F);
+        b = s > b ? s : b;
+    }
+    if (x_dtype != DT_F32 && w_dtype == DT_INT4 && !ffn_small_eligible(T, H, F) && ffn_gemm_q4_eligible(T, K, E, H, F)) {
+        const size_t s = ffn_gemm_q4_workspace_bytes(T, K, E, H, F);
         b = s > b ? s : b;
     }
     return b;
@@ -369,6 +372,9 @@ hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, c
                                 y_dtype == DT_BF16, ws, st);
     if (w_dtype == DT_BF16 && ffn_gemm_eligible(T, K, H, F))
         return launch_ffn_gemm(x, wg, wu, wd, offsets, perm, T, K, H, F, E, y, y_dtype == DT_BF16, ws, st);
+    if (w_dtype == DT_INT4 && ffn_gemm_q4_eligible(T, K, E, H, F))
+        return launch_ffn_gemm_q4(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_dtype == DT_BF16, ws,
+                                  st);
     uint16_t* abuf = (uint16_t*)ws;
     const int tiles_g = (n + G_BM - 1) / G_BM + (E < n ? E : n);
     const int tiles_d = (n + D_BM - 1) / D_BM + (E < n ? E : n);

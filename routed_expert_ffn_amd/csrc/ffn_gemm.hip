@@ -386,6 +386,33 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     }
 }
 
+// int4 weights at prefill: every expert's matrices are expanded once per call
+// into bf16 (value d (u - 8) rounded to bf16 by RNE: the product of the fp16
+// scale and the 4-bit integer is exact in fp32, so this is the only rounding)
+// and the bf16 GEMMs run on the copy.  One thread per quant block (16 bytes of
+// nibbles -> 32 bf16, 64 bytes).
+__global__ __launch_bounds__(256) void k_dequant_q4(const uint8_t* __restrict__ q, const uint16_t* __restrict__ s,
+                                                    long nblocks, uint16_t* __restrict__ out) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nblocks) return;
+    const uint4 w = *reinterpret_cast<const uint4*>(q + i * 16);
+    const float d = fp16_to_f32(s[i]);
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    u32x4_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) {       // byte b of word k: elements 8k+2b (low nibble), 8k+2b+1 (high)
+            const uint32_t byte = (wv[k] >> (8 * b)) & 0xFFu;
+            const float lo = d * (float)((int)(byte & 15u) - 8), hi = d * (float)((int)(byte >> 4) - 8);
+            o[k][b] = cvt_bf16x2(lo, hi);
+        }
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + i * 32);
+#pragma unroll
+    for (int k = 0; k < 4; k++) dst[k] = o[k];
+}
+
 namespace {
 // tile shape per phase: 128 x 512 keeps the row padding of small experts at
 // most 127 rows per expert; both shapes read 128 KB of LDS operands per K step.
@@ -400,6 +427,34 @@ static_assert(GU_BM == PLAN_BM && DN_BM == PLAN_BM, "one tile plan serves both p
 bool ffn_gemm_eligible(int T, int K, int H, int F) {
     return H % DN_BN == 0 && H % BK == 0 && (2 * F) % GU_BN == 0 && F % BK == 0 &&
            (size_t)T * H * 2 < ((size_t)1 << 32) && (size_t)T * K * F * 2 < ((size_t)1 << 32);
+}
+
+// int4 through the bf16 GEMMs: worth the expansion once most experts are touched
+bool ffn_gemm_q4_eligible(int T, int K, int E, int H, int F) {
+    return ffn_gemm_eligible(T, K, H, F) && (long)T * K >= 4L * E && H % 32 == 0 && F % 32 == 0;
+}
+
+static size_t al256g(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace: the bf16 GEMM's, then Wg, Wu, Wd expanded to bf16
+size_t ffn_gemm_q4_workspace_bytes(int T, int K, int E, int H, int F) {
+    return ffn_gemm_workspace_bytes(T, K, E, H, F) + 3 * al256g((size_t)E * F * H * 2);
+}
+
+hipError_t launch_ffn_gemm_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
+                              const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
+                              int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st) {
+    char* wb = (char*)ws + ffn_gemm_workspace_bytes(T, K, E, H, F);
+    const size_t mat = al256g((size_t)E * F * H * 2);
+    uint16_t* g16 = (uint16_t*)wb;
+    uint16_t* u16 = (uint16_t*)(wb + mat);
+    uint16_t* d16 = (uint16_t*)(wb + 2 * mat);
+    const long nb = (long)E * F * H / 32;     // quant blocks per matrix
+    const dim3 grid((unsigned)((nb + 255) / 256));
+    hipLaunchKernelGGL(k_dequant_q4, grid, dim3(256), 0, st, (const uint8_t*)wg, (const uint16_t*)sg, nb, g16);
+    hipLaunchKernelGGL(k_dequant_q4, grid, dim3(256), 0, st, (const uint8_t*)wu, (const uint16_t*)su, nb, u16);
+    hipLaunchKernelGGL(k_dequant_q4, grid, dim3(256), 0, st, (const uint8_t*)wd, (const uint16_t*)sd, nb, d16);
+    return launch_ffn_gemm(x, g16, u16, d16, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
 }
 
 // Workspace: [A n x F bf16][tiles: (n/BM + min(E,n) + 1) x int4][count]

@@ -52,6 +52,11 @@ hipError_t launch_ffn_stream(const void* x, const void* wg, const void* wu, cons
 // ffn_gemm.hip (many rows per expert; bf16 weights)
 bool ffn_gemm_eligible(int T, int K, int H, int F);
 size_t ffn_gemm_workspace_bytes(int T, int K, int E, int H, int F);
+bool ffn_gemm_q4_eligible(int T, int K, int E, int H, int F);
+size_t ffn_gemm_q4_workspace_bytes(int T, int K, int E, int H, int F);
+hipError_t launch_ffn_gemm_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
+                              const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
+                              int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st);
 hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
                            const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                            hipStream_t st);

@@ -78,6 +78,8 @@ SMALL = [
     # tiles, ragged last tile per expert, one item per block)
     synth.LayerShape(T=300, H=512, E=40, K=6, F=256, act="bf16", wdt="bf16", zipf=True),
     synth.LayerShape(T=97, H=1024, E=12, K=3, F=512, act="bf16", wdt="bf16"),
+    # int4, most experts touched: expanded to bf16, then the grouped GEMMs
+    synth.LayerShape(T=300, H=1024, E=16, K=6, F=512, act="bf16", wdt="int4", zipf=True),
     # T <= 16: the weight-streaming path for the verify step
     synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="bf16", zipf=True),
     synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="int4", zipf=True),
@@ -264,6 +266,21 @@ def test_int4_verify_layer_full_size():
     check_routing_and_grouping(r, ref_idx, ref_w, s.E)
     ref_out = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d))
     assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
+def test_int4_prefill_layer_full_size():
+    """One layer of the pruned int4 stack on an 8192-token chunk: the int4 blocks
+    are expanded to bf16 and run through the grouped GEMMs (sampled rows)."""
+    s = synth.STACK_INT4_PREFILL
+    d = synth.make_device_layer(s, seed=0, cfg=5, layer=0, device="cuda")
+    torch.cuda.synchronize()
+    x, wr = to_host(d.x), to_host(d.wr)
+    ref_idx, ref_w, _ = oracle.route(x, wr, s.K)
+    out, r = run_layer(d)
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    rows = np.unique(np.concatenate([[0, s.T - 1], np.random.default_rng(2).choice(s.T, 22, replace=False)]))
+    ref_out = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d), rows=rows)
+    assert row_rel_err(to_host(out)[rows], ref_out) <= TOL_BF16
 
 
 # ---------------------------------------------------------------- prefill chunk, full size
