@@ -104,13 +104,21 @@ MOE_DEV int block_touched_list(const int32_t* __restrict__ offsets, int E, int4*
     return total;
 }
 
-// Copy n_kb KB from global memory to the start of LDS with the LDS DMA, the
-// block's 4 waves taking alternate 1 KB pieces (64 lanes x 16 B each).
-typedef __attribute__((address_space(3))) void lds_void_s;
+// Copy n_kb KB from global memory to the start of LDS, 16 bytes per thread
+// and step, four loads in flight per thread.  Plain loads, not the LDS DMA:
+// the compiler makes every later LDS access in a loop wait for an LDS DMA,
+// which would also wait for the weight prefetch of the streaming loops.
 MOE_DEV void stage_lds(const void* src, int n_kb, unsigned char* lds, int wave, int l) {
-    const unsigned char* g = (const unsigned char*)src + l * 16;
-    for (int i = wave; i < n_kb; i += 4)
-        __builtin_amdgcn_global_load_lds(g + (long)i * 1024, (lds_void_s*)(lds + i * 1024), 16, 0, 0);
+    (void)wave; (void)l;
+    const uint4* g = reinterpret_cast<const uint4*>(src);
+    uint4* d = reinterpret_cast<uint4*>(lds);
+    const int n16 = n_kb * 64;
+    int i = threadIdx.x;
+    for (; i + 3 * 256 < n16; i += 4 * 256) {
+        const uint4 a = g[i], b = g[i + 256], c = g[i + 512], e = g[i + 768];
+        d[i] = a; d[i + 256] = b; d[i + 512] = c; d[i + 768] = e;
+    }
+    for (; i < n16; i += 256) d[i] = g[i];
 }
 
 // A wave's walk over items it, it + W, it + 2W, ... < n: RING weight buffers,
@@ -154,12 +162,10 @@ __global__ __launch_bounds__(256) void k_gateup_stream(const uint16_t* __restric
     int* prow = reinterpret_cast<int*>(list + T * K);                          // [T*K] token of grouped row
     __shared__ int scan[4];
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
-    // the token rows go to LDS by DMA (1 KB per instruction), issued first so
-    // that they land with the offsets the touched list is built from
+    // the token rows go to LDS, then the touched list is built from the offsets
     stage_lds(x, T * H * 2 / 1024, smem, wave, l);
     for (int i = tid; i < T * K; i += 256) prow[i] = perm[i] / K;
     const int nlist = block_touched_list(offsets, E, list, scan);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
 
     const int tpe = F / FR;                     // items per expert
@@ -225,7 +231,6 @@ __global__ __launch_bounds__(256) void k_down_stream(const uint16_t* __restrict_
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
     stage_lds(abuf, nrows * F * 2 / 1024, smem, wave, l);
     const int nlist = block_touched_list(offsets, E, list, scan);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
 
     const int tpe = H / DR;
@@ -347,7 +352,6 @@ __global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __rest
     stage_lds(x, T * H * 2 / 1024, smem, wave, l);
     for (int i = tid; i < T * K; i += 256) prow[i] = perm[i] / K;
     const int nlist = block_touched_list(offsets, E, list, scan);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
     block_sums(xs, T, H, xsum);
     __syncthreads();
@@ -421,7 +425,6 @@ __global__ __launch_bounds__(256) void k_down_stream_q4(const uint16_t* __restri
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
     stage_lds(abuf, nrows * F * 2 / 1024, smem, wave, l);
     const int nlist = block_touched_list(offsets, E, list, scan);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     block_sums(as, nrows, F, asum);
     __syncthreads();
