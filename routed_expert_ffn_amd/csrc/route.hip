@@ -491,19 +491,30 @@ __global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     XT* xs = reinterpret_cast<XT*>(smem);
     const int tid = threadIdx.x;
-    // stage x [T][H] (16-byte copies)
+    const int l = lane_id();
+    // the router row's loads go out first (a wave past E re-reads row E-1),
+    // then x [T][H] is staged with four 16-byte loads in flight per thread
+    const int e = blockIdx.x * 2 + tid / WAVE;
+    const int er = e < E ? e : E - 1;
+    float wf[HL];
+#pragma unroll
+    for (int i = 0; i < HL; i++) wf[i] = wr[(long)er * H + l + i * WAVE];   // H == 64 * HL
+    const float b = bias ? bias[er] : 0.f;
     const int per = 16 / (int)sizeof(XT);
     const int nchunk = T * H / per;
-    for (int i = tid; i < nchunk; i += blockDim.x)
-        reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    const uint4* xg = reinterpret_cast<const uint4*>(x);
+    uint4* xd = reinterpret_cast<uint4*>(xs);
+    int i0 = tid;
+    for (; i0 + 3 * 128 < nchunk; i0 += 4 * 128) {
+        const uint4 a0 = xg[i0], a1 = xg[i0 + 128], a2 = xg[i0 + 256], a3 = xg[i0 + 384];
+        xd[i0] = a0; xd[i0 + 128] = a1; xd[i0 + 256] = a2; xd[i0 + 384] = a3;
+    }
+    for (; i0 < nchunk; i0 += 128) xd[i0] = xg[i0];
     __syncthreads();
-    const int e = blockIdx.x * 2 + tid / WAVE;
     if (e >= E) return;
-    const int l = lane_id();
     double w[HL];
 #pragma unroll
-    for (int i = 0; i < HL; i++) w[i] = (double)wr[(long)e * H + l + i * WAVE];   // H == 64 * HL
-    const float b = bias ? bias[e] : 0.f;
+    for (int i = 0; i < HL; i++) w[i] = (double)wf[i];
     for (int t = 0; t < T; t++) {
         double p = 0.0;
 #pragma unroll
