@@ -19,22 +19,36 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, con
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = 0.f;
-    for (int k = 0; k < K; k++) {
-        const float wk = w[(long)t * K + k];
-        const long row = inv[(long)t * K + k];
-        float v[8];
-        if constexpr (YB) {
-            const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)y + row * H + h);
-            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+    // K routed rows in groups of KB: the group's row loads are all in flight
+    // before its multiply-adds, which run in k order
+    constexpr int KB = 8;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        float v[KB][8];
+        float wk[KB];
 #pragma unroll
-            for (int i = 0; i < 4; i++) { v[2 * i] = bf16lo_to_f32(u[i]); v[2 * i + 1] = bf16hi_to_f32(u[i]); }
-        } else {
-            const float4 a = *reinterpret_cast<const float4*>((const float*)y + row * H + h);
-            const float4 b = *reinterpret_cast<const float4*>((const float*)y + row * H + h + 4);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        for (int u = 0; u < KB; u++) {
+            const int k = min(k0 + u, K - 1);          // past K: re-read the last row (unused)
+            const long row = inv[(long)t * K + k];
+            wk[u] = w[(long)t * K + k];
+            if constexpr (YB) {
+                const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)y + row * H + h);
+                const uint32_t uu[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int i = 0; i < 4; i++) { v[u][2 * i] = bf16lo_to_f32(uu[i]); v[u][2 * i + 1] = bf16hi_to_f32(uu[i]); }
+            } else {
+                const float4 a = *reinterpret_cast<const float4*>((const float*)y + row * H + h);
+                const float4 b = *reinterpret_cast<const float4*>((const float*)y + row * H + h + 4);
+                v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+                v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 8; i++) acc[i] = fmaf(wk, v[i], acc[i]);
+        for (int u = 0; u < KB; u++) {
+            if (k0 + u < K) {                           // uniform
+#pragma unroll
+                for (int i = 0; i < 8; i++) acc[i] = fmaf(wk[u], v[u][i], acc[i]);
+            }
+        }
     }
     const long o = (long)t * H + h;
     if (res) {

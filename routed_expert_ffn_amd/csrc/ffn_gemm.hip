@@ -82,31 +82,55 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 }  // namespace
 
 // Plan: tiles[i] = (expert, first row, rows) for every bm-row tile of every
-// touched expert, in expert order; tiles_count[0] = their number.
+// touched expert, in expert order; tiles_count[0] = their number.  One block:
+// each thread owns 16 consecutive experts (E <= 4096) and loads their offsets
+// at once; the experts' first tile indices go to LDS, and then all threads
+// write the tiles, each finding its tile's expert by binary search.
 __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ offsets, int E, int bm,
                                                    int4* __restrict__ tiles, int32_t* __restrict__ count) {
+    constexpr int EPT = 16;
     __shared__ int wave_tot[4];
-    __shared__ int s_base;
-    if (threadIdx.x == 0) s_base = 0;
+    __shared__ int tstart[256 * EPT + 1];         // first tile of expert e; tstart[E] = total
+    __shared__ int eoff[256 * EPT + 1];           // offsets[e]
+    const int e0 = threadIdx.x * EPT;
+    int off[EPT + 1];
+#pragma unroll
+    for (int i = 0; i <= EPT; i++) off[i] = offsets[min(e0 + i, E)];
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; i++)
+        if (e0 + i < E) t += (off[i + 1] - off[i] + bm - 1) / bm;
+    const int incl = wave_incl_scan(t);
+    const int w = threadIdx.x / WAVE;
+    if (lane_id() == WAVE - 1) wave_tot[w] = incl;
     __syncthreads();
-    for (int e0 = 0; e0 < E; e0 += 256) {
-        const int e = e0 + threadIdx.x;
-        int off = 0, n = 0;
-        if (e < E) { off = offsets[e]; n = offsets[e + 1] - off; }
-        const int t = (n + bm - 1) / bm;
-        const int incl = wave_incl_scan(t);
-        const int w = threadIdx.x / WAVE;
-        if (lane_id() == WAVE - 1) wave_tot[w] = incl;
-        __syncthreads();
-        int before = s_base;
-        for (int i = 0; i < w; i++) before += wave_tot[i];
-        const int start = before + incl - t;
-        for (int j = 0; j < t; j++) tiles[start + j] = make_int4(e, off + j * bm, min(bm, n - j * bm), 0);
-        __syncthreads();
-        if (threadIdx.x == 255) s_base = start + t;
-        __syncthreads();
+    int pos = incl - t;
+    for (int i = 0; i < w; i++) pos += wave_tot[i];
+    const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+#pragma unroll
+    for (int i = 0; i < EPT; i++) {
+        if (e0 + i < E) {
+            tstart[e0 + i] = pos;
+            eoff[e0 + i] = off[i];
+            pos += (off[i + 1] - off[i] + bm - 1) / bm;
+        }
     }
-    if (threadIdx.x == 0) count[0] = s_base;
+    if (threadIdx.x == 0) {
+        tstart[E] = total;
+        eoff[E] = offsets[E];
+        count[0] = total;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < total; i += 256) {
+        int lo = 0, hi = E;                        // largest e with tstart[e] <= i (experts with no tiles share it)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tstart[mid] <= i) lo = mid; else hi = mid;
+        }
+        const int j = i - tstart[lo];
+        const int n = eoff[lo + 1] - eoff[lo];
+        tiles[i] = make_int4(lo, eoff[lo] + j * bm, min(bm, n - j * bm), 0);
+    }
 }
 
 template <int BM, int BN, int PHASE, int YBF16>   // PHASE 0: gate/up (K = H), 1: down (K = F)

@@ -20,7 +20,7 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, float t
                                int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st);
 
 // permute.hip
-constexpr int PERM_CHUNK = 2048;   // slots per grouping block
+constexpr int PERM_CHUNK = 1024;   // slots per grouping block
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                           int32_t* inv, int32_t* chunk_buf, hipStream_t st);
 

@@ -115,40 +115,48 @@ __global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ i
     for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(long)blockIdx.x * E + e] = cnt[e];
 }
 
-// Pass 2 (one block): counts, offsets, and each chunk's first position per expert.
+// Pass 2 (one block): counts, offsets, and each chunk's first position within
+// each expert's segment.
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ chunk_counts, int nchunks, int E,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int* tot = reinterpret_cast<int*>(smem);
     __shared__ int wave_tot[16];
+    // per expert: exclusive prefix over the chunks (16 chunk counts in flight
+    // per thread at a time); the scatter adds the expert's offset
+    constexpr int B = 16;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = 0;
-        for (int c = 0; c < nchunks; c++) {
-            const int v = chunk_counts[(long)c * E + e];
-            chunk_counts[(long)c * E + e] = run;   // exclusive within the expert
-            run += v;
+        for (int c0 = 0; c0 < nchunks; c0 += B) {
+            int v[B];
+#pragma unroll
+            for (int u = 0; u < B; u++) v[u] = chunk_counts[(long)min(c0 + u, nchunks - 1) * E + e];
+#pragma unroll
+            for (int u = 0; u < B; u++)
+                if (c0 + u < nchunks) {
+                    chunk_counts[(long)(c0 + u) * E + e] = run;
+                    run += v[u];
+                }
         }
         counts[e] = run;
         tot[e] = run;
     }
     __syncthreads();
     const int total = block_exclusive_scan(tot, E, wave_tot);
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        offsets[e] = tot[e];
-        for (int c = 0; c < nchunks; c++) chunk_counts[(long)c * E + e] += tot[e];
-    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = tot[e];
     if (threadIdx.x == 0) offsets[E] = total;
 }
 
 // Pass 3: stable scatter, one wave per chunk.
 __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ idx, int n, int E,
                                                      const int32_t* __restrict__ chunk_base,
+                                                     const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
     int* cur = reinterpret_cast<int*>(mask + E);
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        cur[e] = chunk_base[(long)blockIdx.x * E + e];
+        cur[e] = offsets[e] + chunk_base[(long)blockIdx.x * E + e];
         mask[e] = 0ull;
     }
     __syncthreads();
@@ -167,6 +175,7 @@ hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* counts, int
     hipLaunchKernelGGL(k_perm_hist, dim3(nchunks), dim3(256), (size_t)E * sizeof(int), st, idx, n, E, chunk_buf);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), (size_t)E * sizeof(int), st, chunk_buf, nchunks, E, counts,
                        offsets);
-    hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(64), lds_ms, st, idx, n, E, chunk_buf, perm, inv);
+    hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(64), lds_ms, st, idx, n, E, chunk_buf, offsets, perm,
+                       inv);
     return hipGetLastError();
 }
