@@ -8,9 +8,10 @@
 // "专家配置文件：48 x 256 的全量排名").
 //
 //   k_freq_count  top-K of every logit row (routing's rule: larger first, ties
-//                 to the lower id; the same wave selection as routing's),
-//                 per-block LDS histogram, int64 totals via integer atomics
-//                 (exact and order-independent).
+//                 to the lower id), per-block LDS histogram, int64 totals via
+//                 integer atomics (exact and order-independent).  Wide rows
+//                 take a threshold pass first (below); narrow ones, and rows
+//                 the threshold does not settle, use routing's wave selection.
 //   k_freq_rank   per layer: rank_of[e] = number of experts ahead of e in
 //                 (count desc, id asc) order; keep_map = ids of rank < keep in
 //                 ascending id order.
@@ -61,6 +62,126 @@ __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ lo
         if (hist[e]) atomicAdd(&counts[(long)layer * E + e], (unsigned long long)hist[e]);
 }
 
+// Wide rows (E > 128): only the SET of the K winners matters for the counts,
+// so a row is first cut at a threshold value th carried over from the rows
+// before it (all rows of a wave belong to one layer).  If c, the number of
+// values >= th, lies in [K, 64], every winner is among those c candidates
+// (the K-th largest value is >= th), so they are packed into one slot per
+// lane in expert order, and each candidate's rank is the number of others
+// with a larger (order key, lower slot) pair -- one 64-bit compare per
+// candidate, no branches.  The K candidates of rank < K are the winners.
+// Any other row takes routing's selection, whose K-th and first values then
+// reset th (the K-th value minus their spread) and its adjustment step; after
+// a cut row th moves by the step to keep c within [K + 4, 48].  The
+// threshold only decides which exact method runs, never the result (a NaN
+// is never a candidate; NaN rows are unspecified, as in routing).
+constexpr int THR_MAX = 64;
+constexpr int FR_RING = 2;
+template <int VPL>
+__global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict__ logits, int64_t T, int E, int K,
+                                                        int64_t rows_per_layer_blocks,
+                                                        unsigned long long* __restrict__ counts) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned long long* comp_all = reinterpret_cast<unsigned long long*>(smem);   // [4][64] candidate ranks keys
+    float* cval_all = reinterpret_cast<float*>(comp_all + 4 * THR_MAX);          // [4][64] candidate values
+    int* cid_all = reinterpret_cast<int*>(cval_all + 4 * THR_MAX);               // [4][64] candidate experts
+    int* hist = cid_all + 4 * THR_MAX;                                           // [E]
+    const int layer = blockIdx.y;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int wave = threadIdx.x / WAVE, l = lane_id();
+    unsigned long long* comp = comp_all + wave * THR_MAX;
+    float* cval = cval_all + wave * THR_MAX;
+    int* cid = cid_all + wave * THR_MAX;
+    const float* base = logits + (long)layer * T * E;
+    const int64_t step_rows = rows_per_layer_blocks * 4;
+    int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    auto load = [&](int64_t row, float (&v)[VPL]) __attribute__((always_inline)) {
+        const float* r = base + (row < T ? row : T - 1) * E;   // past the end: re-read the last row (unused)
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int e = l + j * WAVE;
+            v[j] = __builtin_nontemporal_load(r + (e < E ? e : E - 1));
+        }
+    };
+    bool have = false;        // wave-uniform threshold state
+    float th = 0.f, th_step = 0.f;
+    auto process = [&](const float (&cur)[VPL]) __attribute__((always_inline)) {
+        auto valid = [&](int j) __attribute__((always_inline)) { return l + j * WAVE < E; };
+        int c = 0;
+        if (have) {
+#pragma unroll
+            for (int j = 0; j < VPL; j++) c += __popcll(__ballot(valid(j) && cur[j] >= th));
+        }
+        c = __builtin_amdgcn_readfirstlane(c);
+        if (have && c >= K && c <= THR_MAX) {
+            int pos0 = 0;
+#pragma unroll
+            for (int j = 0; j < VPL; j++) {
+                const bool in = valid(j) && cur[j] >= th;
+                const unsigned long long m = __ballot(in);
+                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (in) {
+                    cval[pos0 + below] = cur[j];
+                    cid[pos0 + below] = l + j * WAVE;
+                }
+                pos0 += __popcll(m);
+            }
+            __builtin_amdgcn_wave_barrier();
+            // slot l's composite: order key (the float order of non-NaN values,
+            // -0 == +0), then the lower slot (= lower expert); 0 past c
+            const int me = cid[l];
+            const unsigned long long mine =
+                l < c ? ((unsigned long long)f32_order_key(cval[l]) << 32) | (uint32_t)(WAVE - 1 - l) : 0ull;
+            comp[l] = mine;
+            __builtin_amdgcn_wave_barrier();
+            int rank = 0;
+            for (int j = 0; j < c; j += 2) {
+                const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(comp + j);   // the same 16 B for every lane
+                rank += q.x > mine ? 1 : 0;
+                rank += q.y > mine ? 1 : 0;
+            }
+            if (l < c && rank < K) atomicAdd(&hist[me], 1);
+            if (c < K + 4) th -= th_step;
+            else if (c > 48) th += th_step;
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            uint32_t kv[VPL];
+#pragma unroll
+            for (int j = 0; j < VPL; j++) kv[j] = valid(j) ? f32_order_key(cur[j]) : 0u;
+            uint32_t key;
+            int e;
+            select_top<VPL>(kv, K, key, e);
+            if (l < K && e >= 0) atomicAdd(&hist[e], 1);   // e < 0 only if keys ran out (NaN rows)
+            const float v1 = order_key_value(__shfl(key, 0, WAVE));
+            const float vk = order_key_value(__shfl(key, K - 1, WAVE));
+            const float sp = v1 - vk;
+            have = __builtin_isfinite(vk) && __builtin_isfinite(sp) && sp > 0.f && __builtin_isfinite(vk - sp);
+            th = vk - sp;
+            th_step = 0.25f * sp;
+        }
+    };
+    // ring of FR_RING row buffers: FR_RING - 1 rows in flight while one is selected
+    float rb[FR_RING][VPL];
+#pragma unroll
+    for (int b = 0; b < FR_RING - 1; b++) load(t + b * step_rows, rb[b]);
+    bool more = t < T;
+    while (more) {
+#pragma unroll
+        for (int b = 0; b < FR_RING; b++) {
+            if (more) {
+                load(t + (FR_RING - 1) * step_rows, rb[(b + FR_RING - 1) % FR_RING]);
+                process(rb[b]);
+                t += step_rows;
+                more = t < T;
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        if (hist[e]) atomicAdd(&counts[(long)layer * E + e], (unsigned long long)hist[e]);
+}
+
 __global__ __launch_bounds__(256) void k_freq_zero(unsigned long long* __restrict__ counts, long n) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) counts[i] = 0ull;
@@ -94,9 +215,19 @@ __global__ __launch_bounds__(256) void k_freq_rank(const unsigned long long* __r
 template <int VPL>
 static void count_dispatch(const float* logits, int L, int64_t T, int E, int K, unsigned long long* counts,
                            hipStream_t st) {
+    // grid-stride over rows, histogram flushed once per block: about 6144
+    // blocks in all (a few per CU at a time), at least one per layer
     int64_t blocks = (T + 3) / 4;
-    if (blocks > 1024) blocks = 1024;      // grid-stride over rows; histogram flushed once per block
+    const int64_t cap = (6144 + L - 1) / L;
+    if (blocks > cap) blocks = cap;
     dim3 grid((unsigned)blocks, L);
+    if constexpr (VPL >= 4 && VPL <= 16) {
+        if (K <= THR_MAX) {
+            const size_t lds = (size_t)4 * THR_MAX * 16 + (size_t)E * sizeof(int);
+            hipLaunchKernelGGL(k_freq_count_thr<VPL>, grid, dim3(256), lds, st, logits, T, E, K, blocks, counts);
+            return;
+        }
+    }
     hipLaunchKernelGGL(k_freq_count<VPL>, grid, dim3(256), (size_t)E * sizeof(int), st, logits, T, E, K, blocks,
                        counts);
 }

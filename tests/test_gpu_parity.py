@@ -327,6 +327,24 @@ def test_freq_small_with_ties_and_accumulate():
     assert np.array_equal(to_host(c2), ref_c) and np.array_equal(to_host(km2), ref_k)
 
 
+def test_freq_threshold_cut_rows_with_ties():
+    """Wide rows with several rows per wave, so the threshold cut runs next to
+    the full selection: plain Zipf rows, rows on a 0.25 grid (many exact
+    ties at the cut), and a layer mixing constant rows (every key equal)
+    with ordinary ones and occasional far outliers."""
+    L, T, E, K, keep = 3, 40000, 300, 10, 150
+    lg = synth.make_host_logits(L, T, E, seed=3, cfg=4, zipf=True)
+    lg[1] = np.round(lg[1] * 4.0) / 4.0
+    lg[2, ::7] = 1.5
+    lg[2, 3::11, 17] = 40.0
+    ref_c, ref_r, ref_k = oracle.expert_freq(lg, K, keep=keep)
+    c, rk, km = moe.expert_freq(torch.from_numpy(lg).cuda(), K, keep=keep)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(c), ref_c)
+    assert np.array_equal(to_host(rk), ref_r) and np.array_equal(to_host(km), ref_k)
+    assert np.all(to_host(c).sum(axis=1) == T * K)
+
+
 def test_freq_full_size_two_layers_and_invariants():
     T, E, K, keep = synth.FREQ_T, synth.FREQ_E, synth.FREQ_K, synth.FREQ_KEEP
     L = 2
