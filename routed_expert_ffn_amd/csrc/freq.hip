@@ -71,8 +71,8 @@ __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ lo
 // with a larger (order key, lower slot) pair -- one 64-bit compare per
 // candidate, no branches.  The K candidates of rank < K are the winners.
 // Any other row takes routing's selection, whose K-th and first values then
-// reset th (the K-th value minus their spread) and its adjustment step; after
-// a cut row th moves by the step to keep c within [K + 4, 48].  The
+// reset th (the K-th value minus 3/4 of their spread) and its adjustment
+// step; after a cut row th moves by the step to keep c within [K + 3, 28].  The
 // threshold only decides which exact method runs, never the result (a NaN
 // is never a candidate; NaN rows are unspecified, as in routing).
 constexpr int THR_MAX = 64;
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict_
                 rank += q.y > mine ? 1 : 0;
             }
             if (l < c && rank < K) atomicAdd(&hist[me], 1);
-            if (c < K + 4) th -= th_step;
-            else if (c > 48) th += th_step;
+            if (c < K + 3) th -= th_step;
+            else if (c > 28) th += th_step;
             __builtin_amdgcn_wave_barrier();
         } else {
             uint32_t kv[VPL];
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict_
             const float vk = order_key_value(__shfl(key, K - 1, WAVE));
             const float sp = v1 - vk;
             have = __builtin_isfinite(vk) && __builtin_isfinite(sp) && sp > 0.f && __builtin_isfinite(vk - sp);
-            th = vk - sp;
-            th_step = 0.25f * sp;
+            th = vk - 0.75f * sp;
+            th_step = 0.125f * sp;
         }
     };
     // ring of FR_RING row buffers: FR_RING - 1 rows in flight while one is selected
@@ -215,10 +215,10 @@ __global__ __launch_bounds__(256) void k_freq_rank(const unsigned long long* __r
 template <int VPL>
 static void count_dispatch(const float* logits, int L, int64_t T, int E, int K, unsigned long long* counts,
                            hipStream_t st) {
-    // grid-stride over rows, histogram flushed once per block: about 6144
-    // blocks in all (a few per CU at a time), at least one per layer
+    // grid-stride over rows, histogram flushed once per block: about 12288
+    // blocks in all (a few rounds of the CUs), at least one per layer
     int64_t blocks = (T + 3) / 4;
-    const int64_t cap = (6144 + L - 1) / L;
+    const int64_t cap = (12288 + L - 1) / L;
     if (blocks > cap) blocks = cap;
     dim3 grid((unsigned)blocks, L);
     if constexpr (VPL >= 4 && VPL <= 16) {
