@@ -5,18 +5,18 @@
 //   down:     Y = A_e Wd_e^T         (K = F)                              -> y_perm[p][h]
 // (expert = gate/up/down matrices, "Strata Coder 编程模型深度剖析" §3).
 //
-// MFMA-bound at prefill (an 8192-token chunk is ~465 flop per weight byte),
-// so the kernel is built around the bf16 MFMA 16x16x32 with one wave per SIMD:
-//   * block tile BM x BN (256 x 256 or 128 x 512), K step 64; each of the 4
-//     waves owns a 128 x 128 sub-tile (64 MFMA tiles, 256 fp32 accumulators),
-//     the largest a wave can hold, which minimises LDS operand traffic per MFMA;
+// At prefill an 8192-token chunk is ~465 flop per weight byte, so the kernel
+// is built around the bf16 MFMA 32x32x16 with one wave per SIMD:
+//   * block tile BM x BN = 128 x 512, K step 64; each of the 4 waves owns a
+//     128 x 128 sub-tile (4 x 4 MFMA tiles, 256 fp32 accumulators), the
+//     largest a wave holds, which minimises LDS operand traffic per MFMA;
 //   * global -> LDS with the gfx950 LDS DMA (global_load_lds_dwordx4), two LDS
-//     stages; the operand fragments are prefetched from LDS into registers one
-//     half-step ahead, so LDS reads and the next stage's DMA both run under the
-//     MFMAs and one barrier per K step suffices;
+//     stages of 80 KB; the operand fragments are prefetched from LDS into
+//     registers one half-step ahead, so LDS reads and the next stage's DMA
+//     both run under the MFMAs and one barrier per K step suffices;
 //   * LDS rows are 128 B with the 16-byte chunks XOR-swizzled by (row & 7), so
-//     the MFMA operand reads (16 rows x 16 B per lane group) hit distinct
-//     banks; the swizzle is applied on the global side of the DMA;
+//     the MFMA operand reads hit distinct banks; the swizzle is applied on the
+//     global side of the DMA;
 //   * the MFMA is issued with the weight fragment as its first operand, so a
 //     lane's accumulators are 4 consecutive output columns of one row: the
 //     epilogue packs them to bf16 and stages each wave's tile through LDS for
@@ -28,6 +28,10 @@
 //     (m-tile, n-tile) with n fastest, and consecutive work items are kept on
 //     one XCD (blocks are dealt round-robin over the 8 XCDs) so the tiles that
 //     share weights and activation rows share an L2.
+// The kernel is bound by filling LDS (L2 misses and the per-step barrier
+// that the shared A rows need), not by MFMA issue.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -36,26 +40,33 @@ namespace {
 constexpr int BK = 64;
 constexpr int NWAVE = 4;
 
-template <int BM, int BN>
+template <int BM, int BN, int WQ>
 struct Geo {
     static constexpr int WM = BM / 128, WN = BN / 128;      // waves along rows / columns
     static_assert(WM * WN == NWAVE, "4 waves of 128 x 128");
     static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BN * BK * 2;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int BQ_BYTES = WQ ? BN * BK / 2 : BN * BK * 2;   // B rows: bf16, or int4 nibbles
+    static constexpr int BS_BYTES = WQ ? BN * 4 : 0;                  // int4: a row's two fp16 scales per K step
+    static constexpr int STAGE = A_BYTES + BQ_BYTES + BS_BYTES;
     static constexpr int DMA_A = A_BYTES / 1024 / NWAVE;     // 1 KB DMA instructions per wave per stage
-    static constexpr int DMA_B = B_BYTES / 1024 / NWAVE;
-    static constexpr int DMA = DMA_A + DMA_B;
-    static constexpr int LDS = 2 * STAGE;
-    // the epilogue stages each wave's tile through a quarter of stage 1
-    static_assert(STAGE / NWAVE >= 128 * 144 && STAGE / NWAVE >= 64 * 272 && STAGE / NWAVE >= 32 * 528,
-                  "epilogue staging fits a quarter stage");
+    static constexpr int DMA_B = BQ_BYTES / 1024 / NWAVE;
+    static constexpr int DMA_S = BS_BYTES / 256 / NWAVE;     // 4-byte DMA: 256 B per instruction
+    static constexpr int DMA = DMA_A + DMA_B + DMA_S;
+    static_assert(DMA_A * 1024 * NWAVE == A_BYTES && DMA_B * 1024 * NWAVE == BQ_BYTES &&
+                  DMA_S * 256 * NWAVE == BS_BYTES, "whole DMA instructions per wave");
+    // the epilogue stages each wave's tile (at most 128 rows x 144 B) after stage 0
+    static constexpr int EPI_WAVE = 128 * 144;
+    static_assert(EPI_WAVE >= 64 * 272 && EPI_WAVE >= 32 * 528, "epilogue staging sizes");
+    static constexpr int LDS = 2 * STAGE > STAGE + NWAVE * EPI_WAVE ? 2 * STAGE : STAGE + NWAVE * EPI_WAVE;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 MOE_DEV void dma16(const void* g, lds_void* l) {
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+MOE_DEV void dma4(const void* g, lds_void* l) {
+    __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) / lgkmcnt(0), the other counters left alone (gfx9 encoding)
@@ -78,6 +89,19 @@ MOE_DEV uint32_t cvt_bf16x2(float lo, float hi) {
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 int4 weights of one quant block (element 2b in the low nibble of byte b)
+// -> bf16 RNE of d (u - 8): fma(u, d, -8d) rounds the exact product once
+// (u d and 8 d are exact in fp32), the same value as the fp32 product.
+MOE_DEV bf16x8_t q4x8_bf16(uint32_t w, float d) {
+    const float m8 = -8.0f * d;
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    u32x4_t o;
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+        o[b] = cvt_bf16x2(fmaf((float)((lo >> (8 * b)) & 0xFFu), d, m8), fmaf((float)((hi >> (8 * b)) & 0xFFu), d, m8));
+    return __builtin_bit_cast(bf16x8_t, o);
+}
 
 }  // namespace
 
@@ -133,12 +157,16 @@ __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ o
     }
 }
 
-template <int BM, int BN, int PHASE, int YBF16>   // PHASE 0: gate/up (K = H), 1: down (K = F)
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, const uint16_t* __restrict__ w0,
-                                              const uint16_t* __restrict__ w1, const int4* __restrict__ tiles,
+// WQ 1: int4 weights (nibbles + fp16 scale per 32 along K), staged in LDS as
+// they are and turned into the bf16 MFMA operand in registers, right before
+// its MFMAs; the values are the bf16 RNE of d (u - 8).
+template <int BM, int BN, int PHASE, int YBF16, int WQ>   // PHASE 0: gate/up (K = H), 1: down (K = F)
+__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, const void* __restrict__ w0,
+                                              const void* __restrict__ w1, const uint16_t* __restrict__ s0,
+                                              const uint16_t* __restrict__ s1, const int4* __restrict__ tiles,
                                               const int32_t* __restrict__ tile_count, const int32_t* __restrict__ perm,
                                               int topk, int H, int F, void* __restrict__ out) {
-    using G = Geo<BM, BN>;
+    using G = Geo<BM, BN, WQ>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int KD = PHASE == 0 ? H : F;                       // reduction length
     const int NT = PHASE == 0 ? (2 * F) / BN : H / BN;       // n-tiles per m-tile
@@ -162,9 +190,13 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     // are a wave-uniform base plus a 32-bit per-lane byte offset.
     const int dma_row = l >> 3, dma_slot = l & 7;
     const unsigned char* src_b = (const unsigned char*)src;
-    // B: the 8 rows of one instruction are consecutive weight rows (and all gate
-    // or all up), so one lane offset serves every instruction
-    const uint32_t b_off = (uint32_t)dma_row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ dma_row) * 16);
+    // B: the rows of one instruction are consecutive weight rows (and all gate
+    // or all up), so one lane offset serves every instruction.  bf16: 8 rows x
+    // 128 B; int4: 32 rows x 32 B of nibbles (lane -> row l/2, 16-B chunk l&1,
+    // swizzled by bit 3 of the row), and the scales 64 rows x 4 B.
+    const uint32_t b_off = WQ ? (uint32_t)(l >> 1) * (uint32_t)(KD / 2) + (uint32_t)((((l & 1) ^ ((l >> 4) & 1))) * 16)
+                              : (uint32_t)dma_row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ dma_row) * 16);
+    const uint32_t s_off = (uint32_t)l * (uint32_t)(KD / 16);       // int4: scale row pitch KD/32 x 2 B
     struct Item { int e, row0, rows, nt; };
     auto item_of = [&](int it) __attribute__((always_inline)) -> Item {
         const int4 tl = tiles[it / NT];
@@ -182,15 +214,26 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
             a_off[i] = row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ (r & 7)) * 16);
         }
     };
-    auto b_base = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
-        const int n0 = (wave * G::DMA_B + i) * 8;               // first B tile row of instruction i
+    // weight row of B tile row n (n a multiple of 8): its index in matrix `mat`
+    auto b_row = [&](const Item& c, int n0, int& mat) __attribute__((always_inline)) -> long {
         if constexpr (PHASE == 0) {
             const int q = n0 & 127;                              // per 128 rows: 64 gate rows, the same 64 up rows
-            const long f = (long)c.e * F + c.nt * (BN / 2) + (n0 >> 7) * 64 + (q & 63);
-            return (const unsigned char*)(q < 64 ? w0 : w1) + f * KD * 2;
+            mat = q < 64 ? 0 : 1;
+            return (long)c.e * F + c.nt * (BN / 2) + (n0 >> 7) * 64 + (q & 63);
         } else {
-            return (const unsigned char*)w0 + ((long)c.e * H + c.nt * BN + n0) * KD * 2;
+            mat = 0;
+            return (long)c.e * H + c.nt * BN + n0;
         }
+    };
+    auto b_base = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
+        int mat;
+        const long r = b_row(c, (wave * G::DMA_B + i) * (WQ ? 32 : 8), mat);
+        return (const unsigned char*)(mat ? w1 : w0) + r * (WQ ? KD / 2 : KD * 2);
+    };
+    auto s_base = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
+        int mat;
+        const long r = b_row(c, (wave * G::DMA_S + i) * 64, mat);
+        return (const unsigned char*)(mat ? s1 : s0) + r * (KD / 16);
     };
     auto issue = [&](const Item& c, int k) __attribute__((always_inline)) {
         unsigned char* st = smem + (k & 1) * G::STAGE;
@@ -199,40 +242,74 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
             dma16(src_b + k * BK * 2 + a_off[i], (lds_void*)(st + (wave * G::DMA_A + i) * 1024));
 #pragma unroll
         for (int i = 0; i < G::DMA_B; i++)
-            dma16(b_base(c, i) + k * BK * 2 + b_off, (lds_void*)(st + G::A_BYTES + (wave * G::DMA_B + i) * 1024));
+            dma16(b_base(c, i) + k * (WQ ? BK / 2 : BK * 2) + b_off,
+                  (lds_void*)(st + G::A_BYTES + (wave * G::DMA_B + i) * 1024));
+#pragma unroll
+        for (int i = 0; i < G::DMA_S; i++)
+            dma4(s_base(c, i) + k * 4 + s_off,
+                 (lds_void*)(st + G::A_BYTES + G::BQ_BYTES + (wave * G::DMA_S + i) * 256));
     };
 
     // ---- operand fragments of one K half (32) for the 32x32x16 MFMA: 4 row
-    // tiles of A and 4 column tiles of B, each as two K=16 slices
+    // tiles of A and 4 column tiles of B, each as two K=16 slices.  Slice q of
+    // lane half fh holds the 8 k values at chunk kk*4 + q*2 + fh (bf16), or at
+    // chunk kk*4 + fh*2 + q (int4: a lane's 16 consecutive nibbles then feed
+    // both slices); A and B use the same order, so the sum is over the same k.
     const int fr = l & 31, fh = l >> 5;
-    struct Frag { bf16x8_t a[4][2], b[4][2]; };
+    struct FragBF { bf16x8_t a[4][2], b[4][2]; };
+    struct FragQ { bf16x8_t a[4][2]; u32x2_t nb[4]; float d[4]; };   // B: 16 nibbles + scale per column tile
+    using Frag = typename std::conditional<WQ != 0, FragQ, FragBF>::type;
     auto load_frag = [&](Frag& fragm, int stage, int kk) __attribute__((always_inline)) {
         const unsigned char* st = smem + stage * G::STAGE;
 #pragma unroll
         for (int q = 0; q < 2; q++) {
-            const int c = kk * 4 + q * 2 + fh;
+            const int c = WQ ? kk * 4 + fh * 2 + q : kk * 4 + q * 2 + fh;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int r = wm * 128 + i * 32 + fr;
                 fragm.a[i][q] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((c ^ (r & 7)) * 16));
             }
+            if constexpr (!WQ) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int n = wn * 128 + j * 32 + fr;
+                    fragm.b[j][q] =
+                        *reinterpret_cast<const bf16x8_t*>(st + G::A_BYTES + n * 128 + ((c ^ (n & 7)) * 16));
+                }
+            }
+        }
+        if constexpr (WQ) {
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int n = wn * 128 + j * 32 + fr;
-                fragm.b[j][q] = *reinterpret_cast<const bf16x8_t*>(st + G::A_BYTES + n * 128 + ((c ^ (n & 7)) * 16));
+                fragm.nb[j] = *reinterpret_cast<const u32x2_t*>(st + G::A_BYTES + n * 32 +
+                                                                ((kk ^ ((n >> 3) & 1)) * 16) + fh * 8);
+                fragm.d[j] = fp16_to_f32(*reinterpret_cast<const uint16_t*>(st + G::A_BYTES + G::BQ_BYTES + n * 4 + kk * 2));
             }
         }
     };
     // acc[i][j][v]: output row i*32 + (l & 31), column j*32 + (v/4)*8 + (l >> 5)*4 + v%4 of the wave tile
     f32x16_t acc[4][4];
     auto mma = [&](const Frag& fragm) __attribute__((always_inline)) {
+        if constexpr (!WQ) {
 #pragma unroll
-        for (int q = 0; q < 2; q++)
+            for (int q = 0; q < 2; q++)
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fragm.b[j][q], fragm.a[i][q], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 4; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fragm.b[j][q], fragm.a[i][q], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const bf16x8_t b0 = q4x8_bf16(fragm.nb[j][0], fragm.d[j]);
+                const bf16x8_t b1 = q4x8_bf16(fragm.nb[j][1], fragm.d[j]);
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fragm.a[i][0], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fragm.a[i][1], acc[i][j], 0, 0, 0);
+            }
+        }
     };
     // 16 LDS reads (and, after the barrier, this wave's DMA instructions for
     // the stage two steps ahead) spread over the 32 MFMAs of a K half
@@ -244,25 +321,39 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
         }
     };
     auto interleave_dma = [&]() __attribute__((always_inline)) {
-        static_assert(G::DMA >= 16 && G::DMA <= 32, "1 or 2 DMA instructions per group");
+        if constexpr (G::DMA >= 16) {
+            static_assert(G::DMA <= 32, "1 or 2 DMA instructions per group");
 #pragma unroll
-        for (int q = 0; q < G::DMA - 16; q++) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // 2 VMEM (LDS DMA)
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-        }
+            for (int q = 0; q < G::DMA - 16; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // 2 VMEM (LDS DMA)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            }
 #pragma unroll
-        for (int q = G::DMA - 16; q < 16; q++) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (LDS DMA)
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            for (int q = G::DMA - 16; q < 16; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (LDS DMA)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < G::DMA; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (LDS DMA)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            }
+#pragma unroll
+            for (int q = G::DMA; q < 16; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            }
         }
     };
 
-    // ---- epilogue of one item, staged per wave through the LDS of stage 1
-    // (20 KB a wave) while the next item's first stage loads into stage 0
+    // ---- epilogue of one item, staged per wave through the LDS after stage 0
+    // (18 KB a wave) while the next item's first stage loads into stage 0
     auto epilogue = [&](const Item& c) __attribute__((always_inline)) {
-        unsigned char* ep = smem + G::STAGE + wave * (G::STAGE / NWAVE);
+        unsigned char* ep = smem + G::STAGE + wave * G::EPI_WAVE;
         const int orow0 = wm * 128;                  // wave tile's first row within the block tile
         if constexpr (PHASE == 0) {
             // activation: 128 rows x 64 columns bf16, row stride 144 B (18 KB)
@@ -410,33 +501,6 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     }
 }
 
-// int4 weights at prefill: every expert's matrices are expanded once per call
-// into bf16 (value d (u - 8) rounded to bf16 by RNE: the product of the fp16
-// scale and the 4-bit integer is exact in fp32, so this is the only rounding)
-// and the bf16 GEMMs run on the copy.  One thread per quant block (16 bytes of
-// nibbles -> 32 bf16, 64 bytes).
-__global__ __launch_bounds__(256) void k_dequant_q4(const uint8_t* __restrict__ q, const uint16_t* __restrict__ s,
-                                                    long nblocks, uint16_t* __restrict__ out) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nblocks) return;
-    const uint4 w = *reinterpret_cast<const uint4*>(q + i * 16);
-    const float d = fp16_to_f32(s[i]);
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    u32x4_t o[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-#pragma unroll
-        for (int b = 0; b < 4; b++) {       // byte b of word k: elements 8k+2b (low nibble), 8k+2b+1 (high)
-            const uint32_t byte = (wv[k] >> (8 * b)) & 0xFFu;
-            const float lo = d * (float)((int)(byte & 15u) - 8), hi = d * (float)((int)(byte >> 4) - 8);
-            o[k][b] = cvt_bf16x2(lo, hi);
-        }
-    }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + i * 32);
-#pragma unroll
-    for (int k = 0; k < 4; k++) dst[k] = o[k];
-}
-
 namespace {
 // tile shape per phase: 128 x 512 keeps the row padding of small experts at
 // most 127 rows per expert; both shapes read 128 KB of LDS operands per K step.
@@ -453,33 +517,14 @@ bool ffn_gemm_eligible(int T, int K, int H, int F) {
            (size_t)T * H * 2 < ((size_t)1 << 32) && (size_t)T * K * F * 2 < ((size_t)1 << 32);
 }
 
-// int4 through the bf16 GEMMs: worth the expansion once most experts are touched
+// int4 weights at prefill: the same GEMMs with the nibbles and scales staged in
+// LDS (K steps of 64 = two quant blocks); worth it once most experts are
+// touched by several rows, below that the streaming kernels win.
 bool ffn_gemm_q4_eligible(int T, int K, int E, int H, int F) {
-    return ffn_gemm_eligible(T, K, H, F) && (long)T * K >= 4L * E && H % 32 == 0 && F % 32 == 0;
+    return ffn_gemm_eligible(T, K, H, F) && (long)T * K >= 4L * E && H % BK == 0 && F % BK == 0;
 }
 
-static size_t al256g(size_t b) { return (b + 255) / 256 * 256; }
-
-// Workspace: the bf16 GEMM's, then Wg, Wu, Wd expanded to bf16
-size_t ffn_gemm_q4_workspace_bytes(int T, int K, int E, int H, int F) {
-    return ffn_gemm_workspace_bytes(T, K, E, H, F) + 3 * al256g((size_t)E * F * H * 2);
-}
-
-hipError_t launch_ffn_gemm_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
-                              const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
-                              int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st) {
-    char* wb = (char*)ws + ffn_gemm_workspace_bytes(T, K, E, H, F);
-    const size_t mat = al256g((size_t)E * F * H * 2);
-    uint16_t* g16 = (uint16_t*)wb;
-    uint16_t* u16 = (uint16_t*)(wb + mat);
-    uint16_t* d16 = (uint16_t*)(wb + 2 * mat);
-    const long nb = (long)E * F * H / 32;     // quant blocks per matrix
-    const dim3 grid((unsigned)((nb + 255) / 256));
-    hipLaunchKernelGGL(k_dequant_q4, grid, dim3(256), 0, st, (const uint8_t*)wg, (const uint16_t*)sg, nb, g16);
-    hipLaunchKernelGGL(k_dequant_q4, grid, dim3(256), 0, st, (const uint8_t*)wu, (const uint16_t*)su, nb, u16);
-    hipLaunchKernelGGL(k_dequant_q4, grid, dim3(256), 0, st, (const uint8_t*)wd, (const uint16_t*)sd, nb, d16);
-    return launch_ffn_gemm(x, g16, u16, d16, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
-}
+size_t ffn_gemm_q4_workspace_bytes(int T, int K, int E, int H, int F) { return ffn_gemm_workspace_bytes(T, K, E, H, F); }
 
 // Workspace: [A n x F bf16][tiles: (n/BM + min(E,n) + 1) x int4][count]
 size_t ffn_gemm_workspace_bytes(int T, int K, int E, int H, int F) {
@@ -489,12 +534,12 @@ size_t ffn_gemm_workspace_bytes(int T, int K, int E, int H, int F) {
     return (n * F * 2 + 255) / 256 * 256 + (mt * 16 + 255) / 256 * 256 + 256;
 }
 
-template <int BM, int BN, int PHASE, int YBF16>
-static hipError_t launch_one(int items, hipStream_t st, const uint16_t* src, const uint16_t* w0, const uint16_t* w1,
-                             const int4* tiles, const int32_t* count, const int32_t* perm, int K, int H, int F,
-                             void* out) {
-    auto kern = k_gemm<BM, BN, PHASE, YBF16>;
-    const int lds = Geo<BM, BN>::LDS;
+template <int BM, int BN, int PHASE, int YBF16, int WQ>
+static hipError_t launch_one(int items, hipStream_t st, const uint16_t* src, const void* w0, const void* w1,
+                             const uint16_t* s0, const uint16_t* s1, const int4* tiles, const int32_t* count,
+                             const int32_t* perm, int K, int H, int F, void* out) {
+    auto kern = k_gemm<BM, BN, PHASE, YBF16, WQ>;
+    const int lds = Geo<BM, BN, WQ>::LDS;
     static bool attr = false;     // raising the dynamic LDS limit is per function, once
     if (!attr) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -508,13 +553,15 @@ static hipError_t launch_one(int items, hipStream_t st, const uint16_t* src, con
     if (e != hipSuccess) return e;
     const int cap = ncu / 8 * 8 > 8 ? ncu / 8 * 8 : 8;
     const int grid = (items + 7) / 8 * 8 < cap ? (items + 7) / 8 * 8 : cap;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, src, w0, w1, tiles, count, perm, K, H, F, out);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, src, w0, w1, s0, s1, tiles, count, perm, K, H, F, out);
     return hipSuccess;
 }
 
-hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
-                           const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
-                           hipStream_t st) {
+// plan + gate/up + down; WQ 1: int4 weights with their scales
+template <int WQ>
+static hipError_t gemm_phases(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
+                              const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
+                              int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st) {
     const size_t n = (size_t)T * K;
     const size_t mt = n / PLAN_BM + (size_t)(E < (int)n ? E : (int)n) + 1;
     char* base = (char*)ws;
@@ -523,15 +570,28 @@ hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const 
     int32_t* count = (int32_t*)((char*)tiles + (mt * 16 + 255) / 256 * 256);
     hipLaunchKernelGGL(k_gemm_plan, dim3(1), dim3(256), 0, st, offsets, E, PLAN_BM, tiles, count);
     const int items_g = (int)mt * ((2 * F) / GU_BN), items_d = (int)mt * (H / DN_BN);
-    hipError_t e = launch_one<GU_BM, GU_BN, 0, 1>(items_g, st, (const uint16_t*)x, (const uint16_t*)wg,
-                                                  (const uint16_t*)wu, tiles, count, perm, K, H, F, abuf);
+    const uint16_t *s_g = (const uint16_t*)sg, *s_u = (const uint16_t*)su, *s_d = (const uint16_t*)sd;
+    hipError_t e = launch_one<GU_BM, GU_BN, 0, 1, WQ>(items_g, st, (const uint16_t*)x, wg, wu, s_g, s_u, tiles, count,
+                                                      perm, K, H, F, abuf);
     if (e != hipSuccess) return e;
     if (y_bf16)
-        e = launch_one<DN_BM, DN_BN, 1, 1>(items_d, st, abuf, (const uint16_t*)wd, nullptr, tiles, count, perm, K,
-                                           H, F, y);
+        e = launch_one<DN_BM, DN_BN, 1, 1, WQ>(items_d, st, abuf, wd, nullptr, s_d, nullptr, tiles, count, perm, K, H, F,
+                                               y);
     else
-        e = launch_one<DN_BM, DN_BN, 1, 0>(items_d, st, abuf, (const uint16_t*)wd, nullptr, tiles, count, perm, K,
-                                           H, F, y);
+        e = launch_one<DN_BM, DN_BN, 1, 0, WQ>(items_d, st, abuf, wd, nullptr, s_d, nullptr, tiles, count, perm, K, H, F,
+                                               y);
     if (e != hipSuccess) return e;
     return hipGetLastError();
+}
+
+hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
+                           const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
+                           hipStream_t st) {
+    return gemm_phases<0>(x, wg, wu, wd, nullptr, nullptr, nullptr, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
+}
+
+hipError_t launch_ffn_gemm_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
+                              const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
+                              int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st) {
+    return gemm_phases<1>(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_bf16, ws, st);
 }
