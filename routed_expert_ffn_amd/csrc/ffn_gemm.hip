@@ -158,8 +158,8 @@ __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ o
 }
 
 // WQ 1: int4 weights (nibbles + fp16 scale per 32 along K), staged in LDS as
-// they are and turned into the bf16 MFMA operand in registers, right before
-// its MFMAs; the values are the bf16 RNE of d (u - 8).
+// they are and turned into the bf16 MFMA operand in registers as the
+// fragments are read; the values are the bf16 RNE of d (u - 8).
 template <int BM, int BN, int PHASE, int YBF16, int WQ>   // PHASE 0: gate/up (K = H), 1: down (K = F)
 __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, const void* __restrict__ w0,
                                               const void* __restrict__ w1, const uint16_t* __restrict__ s0,
@@ -256,9 +256,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     // chunk kk*4 + fh*2 + q (int4: a lane's 16 consecutive nibbles then feed
     // both slices); A and B use the same order, so the sum is over the same k.
     const int fr = l & 31, fh = l >> 5;
-    struct FragBF { bf16x8_t a[4][2], b[4][2]; };
-    struct FragQ { bf16x8_t a[4][2]; u32x2_t nb[4]; float d[4]; };   // B: 16 nibbles + scale per column tile
-    using Frag = typename std::conditional<WQ != 0, FragQ, FragBF>::type;
+    struct Frag { bf16x8_t a[4][2], b[4][2]; };
     auto load_frag = [&](Frag& fragm, int stage, int kk) __attribute__((always_inline)) {
         const unsigned char* st = smem + stage * G::STAGE;
 #pragma unroll
@@ -279,37 +277,29 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
             }
         }
         if constexpr (WQ) {
+            // a lane's 16 nibbles of column n (one quant block) and its scale
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int n = wn * 128 + j * 32 + fr;
-                fragm.nb[j] = *reinterpret_cast<const u32x2_t*>(st + G::A_BYTES + n * 32 +
-                                                                ((kk ^ ((n >> 3) & 1)) * 16) + fh * 8);
-                fragm.d[j] = fp16_to_f32(*reinterpret_cast<const uint16_t*>(st + G::A_BYTES + G::BQ_BYTES + n * 4 + kk * 2));
+                const u32x2_t nb = *reinterpret_cast<const u32x2_t*>(st + G::A_BYTES + n * 32 +
+                                                                     ((kk ^ ((n >> 3) & 1)) * 16) + fh * 8);
+                const float d =
+                    fp16_to_f32(*reinterpret_cast<const uint16_t*>(st + G::A_BYTES + G::BQ_BYTES + n * 4 + kk * 2));
+                fragm.b[j][0] = q4x8_bf16(nb[0], d);
+                fragm.b[j][1] = q4x8_bf16(nb[1], d);
             }
         }
     };
     // acc[i][j][v]: output row i*32 + (l & 31), column j*32 + (v/4)*8 + (l >> 5)*4 + v%4 of the wave tile
     f32x16_t acc[4][4];
     auto mma = [&](const Frag& fragm) __attribute__((always_inline)) {
-        if constexpr (!WQ) {
 #pragma unroll
-            for (int q = 0; q < 2; q++)
+        for (int q = 0; q < 2; q++)
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+            for (int i = 0; i < 4; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fragm.b[j][q], fragm.a[i][q], acc[i][j], 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const bf16x8_t b0 = q4x8_bf16(fragm.nb[j][0], fragm.d[j]);
-                const bf16x8_t b1 = q4x8_bf16(fragm.nb[j][1], fragm.d[j]);
-#pragma unroll
-                for (int i = 0; i < 4; i++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fragm.a[i][0], acc[i][j], 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; i++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fragm.a[i][1], acc[i][j], 0, 0, 0);
-            }
-        }
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fragm.b[j][q], fragm.a[i][q], acc[i][j], 0, 0, 0);
     };
     // 16 LDS reads (and, after the barrier, this wave's DMA instructions for
     // the stage two steps ahead) spread over the 32 MFMAs of a K half

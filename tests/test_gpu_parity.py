@@ -78,7 +78,7 @@ SMALL = [
     # tiles, ragged last tile per expert, one item per block)
     synth.LayerShape(T=300, H=512, E=40, K=6, F=256, act="bf16", wdt="bf16", zipf=True),
     synth.LayerShape(T=97, H=1024, E=12, K=3, F=512, act="bf16", wdt="bf16"),
-    # int4, most experts touched: expanded to bf16, then the grouped GEMMs
+    # int4, most experts touched: the grouped GEMMs with int4 operands staged in LDS
     synth.LayerShape(T=300, H=1024, E=16, K=6, F=512, act="bf16", wdt="int4", zipf=True),
     # T <= 16: the weight-streaming path for the verify step
     synth.LayerShape(T=16, H=256, E=40, K=6, F=128, act="bf16", wdt="bf16", zipf=True),
@@ -269,8 +269,8 @@ def test_int4_verify_layer_full_size():
 
 
 def test_int4_prefill_layer_full_size():
-    """One layer of the pruned int4 stack on an 8192-token chunk: the int4 blocks
-    are expanded to bf16 and run through the grouped GEMMs (sampled rows)."""
+    """One layer of the pruned int4 stack on an 8192-token chunk: the grouped
+    GEMMs with each weight rounded once to bf16 from its int4 block (sampled rows)."""
     s = synth.STACK_INT4_PREFILL
     d = synth.make_device_layer(s, seed=0, cfg=5, layer=0, device="cuda")
     torch.cuda.synchronize()
