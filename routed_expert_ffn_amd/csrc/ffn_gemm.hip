@@ -42,8 +42,11 @@ constexpr int NWAVE = 4;
 
 template <int BM, int BN, int WQ>
 struct Geo {
-    static constexpr int WM = BM / 128, WN = BN / 128;      // waves along rows / columns
-    static_assert(WM * WN == NWAVE, "4 waves of 128 x 128");
+    static constexpr int WM = BM / 128, WN = NWAVE / WM;     // waves along rows / columns
+    static_assert(BM == 128 && WM * WN == NWAVE, "4 waves side by side over 128 rows");
+    static constexpr int WCOLS = BN / WN;                    // columns of a wave's tile: 128 or 64
+    static constexpr int JT = WCOLS / 32;                    // its 32-column MFMA tiles
+    static_assert(WCOLS == 128 || WCOLS == 64, "wave tile 128 x 128 or 128 x 64");
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int BQ_BYTES = WQ ? BN * BK / 2 : BN * BK * 2;   // B rows: bf16, or int4 nibbles
     static constexpr int BS_BYTES = WQ ? BN * 4 : 0;                  // int4: a row's two fp16 scales per K step
@@ -54,10 +57,14 @@ struct Geo {
     static constexpr int DMA = DMA_A + DMA_B + DMA_S;
     static_assert(DMA_A * 1024 * NWAVE == A_BYTES && DMA_B * 1024 * NWAVE == BQ_BYTES &&
                   DMA_S * 256 * NWAVE == BS_BYTES, "whole DMA instructions per wave");
-    // the epilogue stages each wave's tile (at most 128 rows x 144 B) after stage 0
-    static constexpr int EPI_WAVE = 128 * 144;
-    static_assert(EPI_WAVE >= 64 * 272 && EPI_WAVE >= 32 * 528, "epilogue staging sizes");
+    // epilogue staging per wave, after stage 0: the activation (128 rows x
+    // WCOLS/2 bf16), y in bf16 (two passes of 64 rows) or fp32 (four of 32);
+    // each row padded by 16 B
+    static constexpr int AST = WCOLS + 16, YST = WCOLS * 2 + 16, FST = WCOLS * 4 + 16;
+    static constexpr int EPI_A = 128 * AST, EPI_Y = 64 * YST, EPI_F = 32 * FST;
+    static constexpr int EPI_WAVE = EPI_A > EPI_Y ? (EPI_A > EPI_F ? EPI_A : EPI_F) : (EPI_Y > EPI_F ? EPI_Y : EPI_F);
     static constexpr int LDS = 2 * STAGE > STAGE + NWAVE * EPI_WAVE ? 2 * STAGE : STAGE + NWAVE * EPI_WAVE;
+    static constexpr int BLOCKS_PER_CU = LDS <= 80 * 1024 ? 2 : 1;   // two blocks share a CU when their LDS fits
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256) void k_gemm_plan(const int32_t* __restrict__ o
 // they are and turned into the bf16 MFMA operand in registers as the
 // fragments are read; the values are the bf16 RNE of d (u - 8).
 template <int BM, int BN, int PHASE, int YBF16, int WQ>   // PHASE 0: gate/up (K = H), 1: down (K = F)
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, const void* __restrict__ w0,
+__global__ __launch_bounds__(256, (Geo<BM, BN, WQ>::BLOCKS_PER_CU)) void k_gemm(const uint16_t* __restrict__ src, const void* __restrict__ w0,
                                               const void* __restrict__ w1, const uint16_t* __restrict__ s0,
                                               const uint16_t* __restrict__ s1, const int4* __restrict__ tiles,
                                               const int32_t* __restrict__ tile_count, const int32_t* __restrict__ perm,
@@ -196,7 +203,6 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     // swizzled by bit 3 of the row), and the scales 64 rows x 4 B.
     const uint32_t b_off = WQ ? (uint32_t)(l >> 1) * (uint32_t)(KD / 2) + (uint32_t)((((l & 1) ^ ((l >> 4) & 1))) * 16)
                               : (uint32_t)dma_row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ dma_row) * 16);
-    const uint32_t s_off = (uint32_t)l * (uint32_t)(KD / 16);       // int4: scale row pitch KD/32 x 2 B
     struct Item { int e, row0, rows, nt; };
     auto item_of = [&](int it) __attribute__((always_inline)) -> Item {
         const int4 tl = tiles[it / NT];
@@ -214,25 +220,30 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
             a_off[i] = row * (uint32_t)(KD * 2) + (uint32_t)((dma_slot ^ (r & 7)) * 16);
         }
     };
-    // weight row of B tile row n (n a multiple of 8): its index in matrix `mat`
-    auto b_row = [&](const Item& c, int n0, int& mat) __attribute__((always_inline)) -> long {
+    // weight row of B tile row n: its index in matrix `mat`.  Gate/up: per
+    // wave tile of WCOLS rows, WCOLS/2 gate rows then the same WCOLS/2 up rows.
+    auto b_row = [&](const Item& c, int n, int& mat) __attribute__((always_inline)) -> long {
         if constexpr (PHASE == 0) {
-            const int q = n0 & 127;                              // per 128 rows: 64 gate rows, the same 64 up rows
-            mat = q < 64 ? 0 : 1;
-            return (long)c.e * F + c.nt * (BN / 2) + (n0 >> 7) * 64 + (q & 63);
+            constexpr int HW = G::WCOLS / 2;
+            const int q = n & (G::WCOLS - 1);
+            mat = q < HW ? 0 : 1;
+            return (long)c.e * F + c.nt * (BN / 2) + (n / G::WCOLS) * HW + (q & (HW - 1));
         } else {
             mat = 0;
-            return (long)c.e * H + c.nt * BN + n0;
+            return (long)c.e * H + c.nt * BN + n;
         }
     };
+    // B DMA groups (8 bf16 rows, 32 int4 rows) never straddle a gate/up half
+    static_assert(G::WCOLS / 2 >= 32, "DMA row groups within one matrix");
     auto b_base = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
         int mat;
         const long r = b_row(c, (wave * G::DMA_B + i) * (WQ ? 32 : 8), mat);
         return (const unsigned char*)(mat ? w1 : w0) + r * (WQ ? KD / 2 : KD * 2);
     };
-    auto s_base = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
+    // int4 scales: 64 rows per instruction, lane l -> row l (per-lane matrix)
+    auto s_lane = [&](const Item& c, int i) __attribute__((always_inline)) -> const unsigned char* {
         int mat;
-        const long r = b_row(c, (wave * G::DMA_S + i) * 64, mat);
+        const long r = b_row(c, (wave * G::DMA_S + i) * 64 + l, mat);
         return (const unsigned char*)(mat ? s1 : s0) + r * (KD / 16);
     };
     auto issue = [&](const Item& c, int k) __attribute__((always_inline)) {
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
                   (lds_void*)(st + G::A_BYTES + (wave * G::DMA_B + i) * 1024));
 #pragma unroll
         for (int i = 0; i < G::DMA_S; i++)
-            dma4(s_base(c, i) + k * 4 + s_off,
+            dma4(s_lane(c, i) + k * 4,
                  (lds_void*)(st + G::A_BYTES + G::BQ_BYTES + (wave * G::DMA_S + i) * 256));
     };
 
@@ -256,7 +267,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     // chunk kk*4 + fh*2 + q (int4: a lane's 16 consecutive nibbles then feed
     // both slices); A and B use the same order, so the sum is over the same k.
     const int fr = l & 31, fh = l >> 5;
-    struct Frag { bf16x8_t a[4][2], b[4][2]; };
+    constexpr int JT = G::JT;
+    struct Frag { bf16x8_t a[4][2], b[JT][2]; };
     auto load_frag = [&](Frag& fragm, int stage, int kk) __attribute__((always_inline)) {
         const unsigned char* st = smem + stage * G::STAGE;
 #pragma unroll
@@ -269,8 +281,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
             }
             if constexpr (!WQ) {
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int n = wn * 128 + j * 32 + fr;
+                for (int j = 0; j < JT; j++) {
+                    const int n = wn * G::WCOLS + j * 32 + fr;
                     fragm.b[j][q] =
                         *reinterpret_cast<const bf16x8_t*>(st + G::A_BYTES + n * 128 + ((c ^ (n & 7)) * 16));
                 }
@@ -279,8 +291,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
         if constexpr (WQ) {
             // a lane's 16 nibbles of column n (one quant block) and its scale
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int n = wn * 128 + j * 32 + fr;
+            for (int j = 0; j < JT; j++) {
+                const int n = wn * G::WCOLS + j * 32 + fr;
                 const u32x2_t nb = *reinterpret_cast<const u32x2_t*>(st + G::A_BYTES + n * 32 +
                                                                      ((kk ^ ((n >> 3) & 1)) * 16) + fh * 8);
                 const float d =
@@ -291,27 +303,41 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
         }
     };
     // acc[i][j][v]: output row i*32 + (l & 31), column j*32 + (v/4)*8 + (l >> 5)*4 + v%4 of the wave tile
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][JT];
     auto mma = [&](const Frag& fragm) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < 2; q++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
+                for (int j = 0; j < JT; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fragm.b[j][q], fragm.a[i][q], acc[i][j], 0, 0, 0);
     };
-    // 16 LDS reads (and, after the barrier, this wave's DMA instructions for
-    // the stage two steps ahead) spread over the 32 MFMAs of a K half
+    // The LDS reads of a K half (8 for A, 2 per B column tile) and, after the
+    // barrier, this wave's DMA instructions for the stage two steps ahead,
+    // spread over the 8 x JT MFMAs of the K half.
     auto interleave = [&]() __attribute__((always_inline)) {
+        if constexpr (JT == 4) {
 #pragma unroll
-        for (int q = 0; q < 16; q++) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            for (int q = 0; q < 16; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+#pragma unroll
+            for (int q = 4; q < 12; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
         }
     };
     auto interleave_dma = [&]() __attribute__((always_inline)) {
-        if constexpr (G::DMA >= 16) {
+        if constexpr (JT == 4 && G::DMA >= 16) {
             static_assert(G::DMA <= 32, "1 or 2 DMA instructions per group");
 #pragma unroll
             for (int q = 0; q < G::DMA - 16; q++) {
@@ -325,76 +351,98 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
             }
-        } else {
+        } else if constexpr (JT == 4) {
 #pragma unroll
             for (int q = 0; q < G::DMA; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (LDS DMA)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
 #pragma unroll
             for (int q = G::DMA; q < 16; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+        } else {
+            static_assert(G::DMA >= 4 && G::DMA <= 12, "one DMA instruction per group");
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+#pragma unroll
+            for (int q = 4; q < G::DMA; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+#pragma unroll
+            for (int q = G::DMA; q < 12; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
     };
 
     // ---- epilogue of one item, staged per wave through the LDS after stage 0
-    // (18 KB a wave) while the next item's first stage loads into stage 0
+    // while the next item's first stage loads into stage 0; rows go out as
+    // 16-byte row-contiguous stores
     auto epilogue = [&](const Item& c) __attribute__((always_inline)) {
         unsigned char* ep = smem + G::STAGE + wave * G::EPI_WAVE;
         const int orow0 = wm * 128;                  // wave tile's first row within the block tile
         if constexpr (PHASE == 0) {
-            // activation: 128 rows x 64 columns bf16, row stride 144 B (18 KB)
+            // activation: 128 rows x WCOLS/2 columns bf16 (gate tile j meets up tile j + JT/2)
+            constexpr int JH = JT / 2, LPR = G::WCOLS / 16, RPI = WAVE / LPR;
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+                for (int j = 0; j < JH; j++)
 #pragma unroll
                     for (int g = 0; g < 4; g++) {
                         u32x2_t v;
                         const f32x16_t& ga = acc[i][j];
-                        const f32x16_t& ua = acc[i][j + 2];
+                        const f32x16_t& ua = acc[i][j + JH];
                         v[0] = cvt_bf16x2(silu_fast(ga[g * 4 + 0]) * ua[g * 4 + 0], silu_fast(ga[g * 4 + 1]) * ua[g * 4 + 1]);
                         v[1] = cvt_bf16x2(silu_fast(ga[g * 4 + 2]) * ua[g * 4 + 2], silu_fast(ga[g * 4 + 3]) * ua[g * 4 + 3]);
-                        *reinterpret_cast<u32x2_t*>(ep + (i * 32 + fr) * 144 + (j * 32 + g * 8 + fh * 4) * 2) = v;
+                        *reinterpret_cast<u32x2_t*>(ep + (i * 32 + fr) * G::AST + (j * 32 + g * 8 + fh * 4) * 2) = v;
                     }
             wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
             uint16_t* A = (uint16_t*)out;
-            const int fc0 = c.nt * (BN / 2) + wn * 64;
+            const int fc0 = c.nt * (BN / 2) + wn * (G::WCOLS / 2);
 #pragma unroll
-            for (int it = 0; it < 16; it++) {        // 8 lanes x 16 B per row, 8 rows per instruction
-                const int r = it * 8 + (l >> 3), cc = l & 7;
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r * 144 + cc * 16);
+            for (int it = 0; it < 128 / RPI; it++) {   // LPR lanes x 16 B per row
+                const int r = it * RPI + l / LPR, cc = l % LPR;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r * G::AST + cc * 16);
                 const int m = orow0 + r;
                 if (m < c.rows) *reinterpret_cast<u32x4_t*>(A + (long)(c.row0 + m) * F + fc0 + cc * 8) = v;
             }
         } else if constexpr (YBF16) {
-            // two passes of 64 rows x 128 columns bf16, row stride 272 B (17 KB)
+            // two passes of 64 rows x WCOLS columns bf16
+            constexpr int LPR = G::WCOLS / 8, RPI = WAVE / LPR;
             uint16_t* Y = (uint16_t*)out;
-            const int h0 = c.nt * BN + wn * 128;
+            const int h0 = c.nt * BN + wn * G::WCOLS;
 #pragma unroll
             for (int half = 0; half < 2; half++) {
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
+                    for (int j = 0; j < JT; j++)
 #pragma unroll
                         for (int g = 0; g < 4; g++) {
                             const f32x16_t& a = acc[half * 2 + i][j];
                             u32x2_t v;
                             v[0] = cvt_bf16x2(a[g * 4 + 0], a[g * 4 + 1]);
                             v[1] = cvt_bf16x2(a[g * 4 + 2], a[g * 4 + 3]);
-                            *reinterpret_cast<u32x2_t*>(ep + (i * 32 + fr) * 272 + (j * 32 + g * 8 + fh * 4) * 2) = v;
+                            *reinterpret_cast<u32x2_t*>(ep + (i * 32 + fr) * G::YST + (j * 32 + g * 8 + fh * 4) * 2) = v;
                         }
                 wait_lgkm0();
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int it = 0; it < 16; it++) {    // 16 lanes x 16 B per row, 4 rows per instruction
-                    const int r = it * 4 + (l >> 4), cc = l & 15;
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r * 272 + cc * 16);
+                for (int it = 0; it < 64 / RPI; it++) {    // LPR lanes x 16 B per row
+                    const int r = it * RPI + l / LPR, cc = l % LPR;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r * G::YST + cc * 16);
                     const int m = orow0 + half * 64 + r;
                     if (m < c.rows) *reinterpret_cast<u32x4_t*>(Y + (long)(c.row0 + m) * H + h0 + cc * 8) = v;
                 }
@@ -402,25 +450,26 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
                 __builtin_amdgcn_wave_barrier();
             }
         } else {
-            // four passes of 32 rows x 128 columns fp32, row stride 528 B (16.5 KB)
+            // four passes of 32 rows x WCOLS columns fp32
+            constexpr int LPR = G::WCOLS / 4, RPI = WAVE / LPR;
             float* Y = (float*)out;
-            const int h0 = c.nt * BN + wn * 128;
+            const int h0 = c.nt * BN + wn * G::WCOLS;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
 #pragma unroll
-                for (int j = 0; j < 4; j++)
+                for (int j = 0; j < JT; j++)
 #pragma unroll
                     for (int g = 0; g < 4; g++) {
                         const f32x16_t& a = acc[i][j];
-                        *reinterpret_cast<f32x4_t*>(ep + fr * 528 + (j * 32 + g * 8 + fh * 4) * 4) =
+                        *reinterpret_cast<f32x4_t*>(ep + fr * G::FST + (j * 32 + g * 8 + fh * 4) * 4) =
                             f32x4_t{a[g * 4 + 0], a[g * 4 + 1], a[g * 4 + 2], a[g * 4 + 3]};
                     }
                 wait_lgkm0();
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int it = 0; it < 16; it++) {    // 32 lanes x 16 B per row, 2 rows per instruction
-                    const int r = it * 2 + (l >> 5), cc = l & 31;
-                    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ep + r * 528 + cc * 16);
+                for (int it = 0; it < 32 / RPI; it++) {    // LPR lanes x 16 B per row
+                    const int r = it * RPI + l / LPR, cc = l % LPR;
+                    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ep + r * G::FST + cc * 16);
                     const int m = orow0 + i * 32 + r;
                     if (m < c.rows) *reinterpret_cast<f32x4_t*>(Y + (long)(c.row0 + m) * H + h0 + cc * 4) = v;
                 }
@@ -435,8 +484,23 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
     issue(cur, 0);
     if (nk > 1) issue(cur, 1);
     Frag f0, f1;
-    // steady state of one item: the first K half multiplies f0 while the second
-    // half of this stage is read into f1; then, once stage k+1 has landed
+    // Two blocks per CU (SB): one fragment set, read just before its MFMAs --
+    // the other block's waves cover the LDS latency -- and one barrier per K
+    // step, after which the drained stage takes the DMA of step k + 2.
+    constexpr bool SB = G::BLOCKS_PER_CU == 2;
+    auto step_sb = [&](int k, bool more) __attribute__((always_inline)) {
+        const int s = k & 1;
+        load_frag(f0, s, 0);
+        mma(f0);
+        load_frag(f0, s, 1);
+        mma(f0);
+        wait_vmcnt<0>();           // this wave's DMA of stage k+1 has landed
+        wait_lgkm0();              // and its reads of stage k are done
+        __builtin_amdgcn_s_barrier();
+        if (more) issue(cur, k + 2);
+    };
+    // One block per CU: the first K half multiplies f0 while the second half
+    // of this stage is read into f1; then, once stage k+1 has landed
     // everywhere, the DMA of k+2 goes into the drained stage and f0 is refilled
     // from k+1 under the second half's MFMAs.  The last two steps are peeled so
     // the loop body has no branches.
@@ -461,20 +525,27 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < JT; j++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
-        load_frag(f0, 0, 0);
-        int k = 0;
-        for (; k + 2 < nk; k++) step(k, true);
-        if (k + 1 < nk) { step(k, false); k++; }
-        load_frag(f1, k & 1, 1);
-        mma(f0);
-        interleave();
-        // every operand of this item is in registers once f1 has arrived: the
-        // LDS is free for the next item's first stage and this item's epilogue
-        wait_lgkm0();
-        __builtin_amdgcn_s_barrier();
+        if constexpr (SB) {
+            int k = 0;
+            for (; k + 2 < nk; k++) step_sb(k, true);
+            for (; k < nk; k++) step_sb(k, false);
+            // the last step's barrier: every wave is done with the LDS
+        } else {
+            load_frag(f0, 0, 0);
+            int k = 0;
+            for (; k + 2 < nk; k++) step(k, true);
+            if (k + 1 < nk) { step(k, false); k++; }
+            load_frag(f1, k & 1, 1);
+            mma(f0);
+            interleave();
+            // every operand of this item is in registers once f1 has arrived: the
+            // LDS is free for the next item's first stage and this item's epilogue
+            wait_lgkm0();
+            __builtin_amdgcn_s_barrier();
+        }
         const Item done = cur;
         item += nslot;
         const bool more = item < item_end;
@@ -483,7 +554,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
             set_a(cur);
             issue(cur, 0);
         }
-        mma(f1);
+        if constexpr (!SB) mma(f1);
         epilogue(done);
         if (!more) break;
         __builtin_amdgcn_s_barrier();       // every wave is done with its staging area (stage 1)
@@ -492,10 +563,14 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ src, 
 }
 
 namespace {
-// tile shape per phase: 128 x 512 keeps the row padding of small experts at
-// most 127 rows per expert; both shapes read 128 KB of LDS operands per K step.
+// tile shape: 128 rows keep the row padding of small experts at most 127 rows
+// per expert.  bf16 weights: 128 x 512 (one block per CU, 160 KB of LDS, the
+// fewest LDS fill bytes per flop); int4 weights: 128 x 256 (57 KB of LDS, two
+// blocks per CU, so one block's operand conversion runs beside the other's
+// MFMAs).
 constexpr int GU_BM = 128, GU_BN = 512;
 constexpr int DN_BM = 128, DN_BN = 512;
+constexpr int Q4_BN = 256;
 constexpr int PLAN_BM = 128;
 static_assert(GU_BM == PLAN_BM && DN_BM == PLAN_BM, "one tile plan serves both phases");
 }  // namespace
@@ -536,12 +611,14 @@ static hipError_t launch_one(int items, hipStream_t st, const uint16_t* src, con
         if (e != hipSuccess) return e;
         attr = true;
     }
-    // persistent: one block per CU (the LDS holds one), a multiple of the 8 XCDs
+    // persistent: as many blocks as the CUs hold at once (one or two per CU,
+    // by LDS), a multiple of the 8 XCDs
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const int cap = ncu / 8 * 8 > 8 ? ncu / 8 * 8 : 8;
+    const int slots = ncu * Geo<BM, BN, WQ>::BLOCKS_PER_CU;
+    const int cap = slots / 8 * 8 > 8 ? slots / 8 * 8 : 8;
     const int grid = (items + 7) / 8 * 8 < cap ? (items + 7) / 8 * 8 : cap;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, src, w0, w1, s0, s1, tiles, count, perm, K, H, F, out);
     return hipSuccess;
@@ -559,17 +636,16 @@ static hipError_t gemm_phases(const void* x, const void* wg, const void* wu, con
     int4* tiles = (int4*)(base + (n * F * 2 + 255) / 256 * 256);
     int32_t* count = (int32_t*)((char*)tiles + (mt * 16 + 255) / 256 * 256);
     hipLaunchKernelGGL(k_gemm_plan, dim3(1), dim3(256), 0, st, offsets, E, PLAN_BM, tiles, count);
-    const int items_g = (int)mt * ((2 * F) / GU_BN), items_d = (int)mt * (H / DN_BN);
+    constexpr int BNG = WQ ? Q4_BN : GU_BN, BND = WQ ? Q4_BN : DN_BN;
+    const int items_g = (int)mt * ((2 * F) / BNG), items_d = (int)mt * (H / BND);
     const uint16_t *s_g = (const uint16_t*)sg, *s_u = (const uint16_t*)su, *s_d = (const uint16_t*)sd;
-    hipError_t e = launch_one<GU_BM, GU_BN, 0, 1, WQ>(items_g, st, (const uint16_t*)x, wg, wu, s_g, s_u, tiles, count,
-                                                      perm, K, H, F, abuf);
+    hipError_t e = launch_one<GU_BM, BNG, 0, 1, WQ>(items_g, st, (const uint16_t*)x, wg, wu, s_g, s_u, tiles, count,
+                                                    perm, K, H, F, abuf);
     if (e != hipSuccess) return e;
     if (y_bf16)
-        e = launch_one<DN_BM, DN_BN, 1, 1, WQ>(items_d, st, abuf, wd, nullptr, s_d, nullptr, tiles, count, perm, K, H, F,
-                                               y);
+        e = launch_one<DN_BM, BND, 1, 1, WQ>(items_d, st, abuf, wd, nullptr, s_d, nullptr, tiles, count, perm, K, H, F, y);
     else
-        e = launch_one<DN_BM, DN_BN, 1, 0, WQ>(items_d, st, abuf, wd, nullptr, s_d, nullptr, tiles, count, perm, K, H, F,
-                                               y);
+        e = launch_one<DN_BM, BND, 1, 0, WQ>(items_d, st, abuf, wd, nullptr, s_d, nullptr, tiles, count, perm, K, H, F, y);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
