@@ -101,7 +101,13 @@ const char* moe_status_string(moe_status s);
  * products x*w taken in wave-64 order (64 strided partial sums, then a pairwise
  * tree 32,16,...,1); the selection is exact with respect to these values.  A
  * faster fp32 estimate is used where every gap among the leading K+1 logits
- * clears a safety margin; other tokens are re-decided on the exact values.
+ * clears a safety margin of 2^-12; other tokens are re-decided on the exact
+ * values.  The estimate (bf16 activations, T >= 64, logits_out NULL) is exact
+ * in every product and rounds only in its fp32 accumulation, so the selection
+ * stays exact while that error stays below half the margin: measured below
+ * 1e-6 for activations ~N(0,1) and router weights ~N(0,0.02) at H = 2048, and
+ * growing in proportion to |x| |w|.  Passing logits_out selects the exact
+ * logits for every token.
  * Unsupported: K > 32, E > 4096, H % 8 != 0.  NaN logits give unspecified
  * selections. */
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype);
