@@ -114,16 +114,19 @@ def test_small_layers_span_tiles(s):
     assert row_rel_err(to_host(out32), ref_out) <= TOL_BF16
 
 
-def test_gemm_path_blocks_walk_several_items():
-    """More 128-row tiles than the chip has CUs: every persistent block of the
-    grouped GEMM handles several (expert, tile) items in turn."""
-    s = synth.LayerShape(T=4096, H=1024, E=16, K=8, F=512, act="bf16", wdt="bf16", zipf=True)
+@pytest.mark.parametrize("wdt", ["bf16", "int4"])
+def test_gemm_path_blocks_walk_several_items(wdt):
+    """More 128-row tiles than the chip holds blocks: every persistent block of
+    the grouped GEMM handles several (expert, tile) items in turn (bf16: 128 x
+    512 tiles, one block per CU; int4: 128 x 256 tiles, two blocks per CU)."""
+    s = synth.LayerShape(T=4096, H=1024, E=16, K=8, F=512, act="bf16", wdt=wdt, zipf=True)
     h = synth.make_host_layer(s, seed=5, cfg=7)
     d = device_from_host(h)
     ref_idx, ref_w, _ = oracle.route(h.x, h.wr, s.K, h.bias)
     counts = np.bincount(ref_idx.ravel(), minlength=s.E)
-    items_per_phase = int(np.sum((counts + 127) // 128)) * 2
-    assert items_per_phase > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    n_tiles, per_cu = (2, 1) if wdt == "bf16" else (4, 2)
+    items_per_phase = int(np.sum((counts + 127) // 128)) * n_tiles
+    assert items_per_phase > 2 * per_cu * torch.cuda.get_device_properties(0).multi_processor_count
     rows = np.unique(np.concatenate([[0, s.T - 1], np.random.default_rng(1).choice(s.T, 62, replace=False)]))
     ref_out = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d), rows=rows)
     for y_dtype in (None, torch.float32):
