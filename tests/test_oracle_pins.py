@@ -429,3 +429,106 @@ def test_bf16_rounding_point_of_the_swiglu_product(orc):
     out = orc.layer_rows(x, np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32),
                          orc.Weights("bf16", wg, wu, wd))
     assert synth.bf16_bits_to_f32(out).tolist() == [[0.078125, 0.0]]
+
+
+# ------------------------------------------------------------------ expert profile (global ranking, STRP, remap, hits)
+def _prof():
+    from oracle import profile
+    return profile
+
+
+def test_profile_rank_brute_force_and_ties():
+    """Rank = number of pairs strictly ahead under (count desc, flat index asc),
+    counted pair by pair, on tiny inputs with many equal counts."""
+    P = _prof()
+    rng = np.random.default_rng(3)
+    for L, E in ((1, 1), (2, 3), (3, 5), (4, 7)):
+        counts = rng.integers(0, 4, size=(L, E))
+        pairs, rank = P.global_rank(counts)
+        for l in range(L):
+            for e in range(E):
+                ahead = sum(1 for l2 in range(L) for e2 in range(E)
+                            if counts[l2, e2] > counts[l, e] or (counts[l2, e2] == counts[l, e] and (l2, e2) < (l, e)))
+                assert rank[l, e] == ahead
+                assert tuple(pairs[ahead]) == (l, e)
+    # invariants on a statistic-sized case: a permutation, counts non-increasing along the ranking
+    counts = rng.integers(0, 50, size=(48, 64))
+    pairs, rank = P.global_rank(counts)
+    assert sorted(rank.reshape(-1).tolist()) == list(range(48 * 64))
+    seq = [counts[l, e] for l, e in pairs.tolist()]
+    assert all(a >= b for a, b in zip(seq, seq[1:]))
+
+
+def test_strp_hand_example_bytes():
+    """STRP v1 written out by hand for 2 layers x 3 experts (counts 5 0 2 / 2 7 0)."""
+    P = _prof()
+    pairs, _ = P.global_rank(np.array([[5, 0, 2], [2, 7, 0]]))
+    # order: (1,1)=7, (0,0)=5, (0,2)=2, (1,0)=2, (0,1)=0, (1,2)=0
+    expect = (b"STRP" + bytes([1, 0, 0, 0, 2, 0, 0, 0, 3, 0, 0, 0, 6, 0, 0, 0, 6, 0, 0, 0])
+              + bytes([1, 0, 1, 0, 0, 0, 0, 0, 0, 0, 2, 0, 1, 0, 0, 0, 0, 0, 1, 0, 1, 0, 2, 0])
+              + bytes([1, 0, 4, 0, 2, 0, 3, 0, 0, 0, 5, 0]))
+    assert P.strp_bytes(pairs, 2, 3) == expect
+    L, E, p2, inv = P.strp_parse(expect)
+    assert (L, E) == (2, 3) and np.array_equal(p2, pairs)
+    assert inv.tolist() == [[1, 4, 2], [3, 0, 5]]
+    with pytest.raises(ValueError):
+        P.strp_parse(expect[:-2])
+    with pytest.raises(ValueError):
+        P.strp_parse(b"STRQ" + expect[4:])
+
+
+def test_strp_round_trip_and_unranked_entries():
+    P = _prof()
+    rng = np.random.default_rng(4)
+    pairs, _ = P.global_rank(rng.integers(0, 9, size=(5, 11)))
+    part = pairs[:20]                                   # a profile may rank only some pairs
+    L, E, p2, inv = P.strp_parse(P.strp_bytes(part, 5, 11))
+    assert np.array_equal(p2, part)
+    assert int((inv >= 0).sum()) == 20 and int((inv == -1).sum()) == 55 - 20
+    for r, (l, e) in enumerate(part.tolist()):
+        assert inv[l, e] == r
+
+
+def test_profile_remap_keeps_order_and_drops_pruned():
+    """A 512-space profile through the keep list: every surviving pair is a kept
+    expert at its position in the list, ranks keep their order, and the number
+    of survivors is the number of ranked pairs whose expert is kept."""
+    P = _prof()
+    rng = np.random.default_rng(5)
+    L, E, keep = 4, 16, 8
+    counts = rng.integers(0, 30, size=(L, E))
+    pairs, rank = P.global_rank(counts)
+    keep_map = np.sort(np.stack([rng.choice(E, keep, replace=False) for _ in range(L)]), axis=1)
+    top = pairs[:40]
+    out = P.remap(top, keep_map)
+    kept = [(l, e) for l, e in top.tolist() if e in set(keep_map[l].tolist())]
+    assert len(out) == len(kept)
+    for (l, j), (l0, e0) in zip(out.tolist(), kept):
+        assert l == l0 and keep_map[l, j] == e0
+    # a keep list of everything is the identity; of nothing leaves an empty profile
+    assert np.array_equal(P.remap(top, np.tile(np.arange(E), (L, 1))), top)
+    assert P.remap(top, np.zeros((L, 0), dtype=np.int64)).shape == (0, 2)
+
+
+def test_profile_hit_rate_closed_forms():
+    """Hit rate of the first S ranked pairs on a trace: a profile built from the
+    trace's own counts reaches the sum of the S largest counts (the most any S
+    pairs can); random profiles average S / (L E); S = 0 and S = L E give 0 and 1."""
+    P = _prof()
+    rng = np.random.default_rng(6)
+    L, T, K, E = 3, 200, 4, 16
+    bias = -1.1 * np.log1p(np.arange(E))
+    trace = np.stack([np.argsort(-(rng.standard_normal((T, E)) + bias), axis=1)[:, :K] for _ in range(L)])
+    counts = np.stack([np.bincount(trace[l].reshape(-1), minlength=E) for l in range(L)])
+    pairs, _ = P.global_rank(counts)
+    for S in (0, 1, 5, 17, L * E):
+        h, n = P.hits(trace, pairs, S)
+        assert n == L * T * K
+        assert h == int(np.sort(counts.reshape(-1))[::-1][:S].sum())
+    assert P.hits(trace, pairs, L * E)[0] == L * T * K
+    S, acc = 12, []
+    for _ in range(400):
+        perm = rng.permutation(L * E)
+        rp = np.stack([perm // E, perm % E], axis=1).astype(np.uint16)
+        acc.append(P.hits(trace, rp, S)[0] / (L * T * K))
+    assert abs(np.mean(acc) - S / (L * E)) < 0.01
