@@ -248,8 +248,39 @@ def bench_freq(torch, moe, synth, steps, warmup, use_graph):
                roofline=dict(bound="hbm", achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=round(a / HBM_PEAK_GBS, 4), kernel="moe_expert_freq",
                              traffic=measured_traffic("freq")))
+    prof = bench_profile(torch, moe, lg, K)
     del lg
-    return res
+    return res, prof
+
+
+def bench_profile(torch, moe, lg, K, slots=2537, n_eval=8192):
+    """The expert profile on the statistic's logits: counts of the first half of
+    the calibration tokens, their global (layer, expert) ranking, and the share
+    of the routed reads of held-out tokens (the second half) that the first
+    `slots` ranked pairs serve, next to the share a profile unrelated to the
+    routing would serve (slots / pairs)."""
+    L, T, E = lg.shape
+    half = T // 2
+    counts = torch.zeros((L, E), dtype=torch.int64, device="cuda")
+    for l in range(L):
+        moe.expert_freq(lg[l, :half], K, counts=counts[l:l + 1])
+    trace = torch.stack([torch.topk(lg[l, half:half + n_eval], K, dim=1).indices.to(torch.int32)
+                         for l in range(L)]).contiguous()
+    ws = torch.empty(moe.load().moe_profile_workspace_size(L, E), dtype=torch.uint8, device="cuda")
+    rank, pairs = moe.profile_rank(counts, workspace=ws)
+    hits = moe.profile_hits(trace, rank, slots)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    reps = 20
+    dt_r, _ = timer.run(lambda: moe.profile_rank(counts, workspace=ws), reps)
+    dt_h, _ = timer.run(lambda: moe.profile_hits(trace, rank, slots), reps)
+    rate = int(hits.item()) / trace.numel()
+    log(f"[profile] rank {dt_r / reps * 1e6:.1f} us, hits {dt_h / reps * 1e6:.1f} us, hit rate of the first {slots} "
+        f"pairs {rate:.3f} (unrelated profile: {slots / (L * E):.3f})")
+    return dict(name=f"expert profile: global rank of {L} x {E} pairs, hit rate of the first {slots} on "
+                     f"{L} x {n_eval} held-out tokens x top-{K}",
+                rank_us=round(dt_r / reps * 1e6, 2), hits_us=round(dt_h / reps * 1e6, 2),
+                hit_rate=round(rate, 4), unrelated_profile_rate=round(slots / (L * E), 4))
 
 
 # ------------------------------------------------------------------ copy (counter calibration)
@@ -356,9 +387,10 @@ def main():
         also.append(r)
         torch.cuda.empty_cache()
     if "freq" in wl:
-        r = bench_freq(torch, moe, synth, max(5, args.steps // 20), 2, use_graph)
+        r, prof = bench_freq(torch, moe, synth, max(5, args.steps // 20), 2, use_graph)
         log(f"[freq] {r['ms_per_step']:.3f} ms/step")
         also.append(r)
+        also.append(prof)
         torch.cuda.empty_cache()
     if "copy" in wl:
         r = bench_copy(torch, args.steps)

@@ -174,6 +174,49 @@ moe_status moe_expert_freq(const float* logits, int32_t L, int64_t T, int32_t E,
                            int64_t* counts, int32_t accumulate, int32_t keep,
                            int32_t* rank_of, int32_t* keep_map, moe_stream stream);
 
+/* ---------------------------------------------------------------- expert profile
+ * The global ranking an engine uses to choose which experts stay in its fast
+ * memory (page 1 §3; the kwkr.cn Coder write-up, "专家配置文件：48 x 256 的全量
+ * 排名": a ranking of every (layer, expert) pair, written as an STRP file,
+ * mapped to the pruned model through its keep list, and checked by the share
+ * of routed reads that hit the first S ranked pairs).
+ *
+ * moe_profile_rank (device): counts [L][E] int64 (e.g. moe_expert_freq's) ->
+ *   rank  [L][E] int32: each pair's position in (count descending, flat index
+ *         layer*E + expert ascending) order;
+ *   pairs [L*E][2] uint16 (4-byte aligned): (layer, expert) in rank order.
+ *   Workspace: moe_profile_workspace_size(L, E) bytes.  Unsupported: E > 4096.
+ * moe_profile_hits (device): trace [L][T][K] int32 expert ids (one routing per
+ *   layer, e.g. moe_route's topk_idx), rank as above -> *hits (uint64, device)
+ *   = the number of trace entries whose pair has rank < S (ids outside [0, E)
+ *   never hit).  The hit rate is *hits / (L*T*K).
+ * STRP v1, host memory, little-endian: "STRP", uint32 version (1), layers,
+ *   experts, ranked pairs n, entries (= layers*experts); n pairs of uint16
+ *   (layer, expert) in rank order; an int16 [layers][experts] table of each
+ *   pair's rank, -1 if unranked.  n <= 32767 (int16 ranks).
+ *   moe_strp_write fills out[moe_strp_size(L, E, n)] from host pairs [n][2]
+ *   (each pair in range and ranked once, else MOE_ERR_INVALID_ARG);
+ *   moe_strp_read checks the header and sizes, sets *L, *E, *n_ranked and, when
+ *   given room (pairs_capacity >= n pairs, inverse_capacity >= L*E entries),
+ *   copies the pairs and the table (NULL skips either).
+ * moe_profile_remap (host): ranked pairs of an E_old-expert profile -> the
+ *   pruned model's: expert e of layer l becomes its position in keep_map[l]
+ *   ([L][keep] int32, ascending ids, e.g. moe_expert_freq's keep_map); pairs
+ *   of pruned experts are dropped and the order is kept; *n_out = survivors.
+ *   out holds up to n pairs. */
+size_t moe_profile_workspace_size(int32_t L, int32_t E);
+moe_status moe_profile_rank(const int64_t* counts, int32_t L, int32_t E, int32_t* rank, uint16_t* pairs,
+                            void* workspace, size_t ws_bytes, moe_stream stream);
+moe_status moe_profile_hits(const int32_t* trace, int32_t L, int64_t T, int32_t K, const int32_t* rank,
+                            int32_t E, int64_t S, uint64_t* hits, moe_stream stream);
+size_t moe_strp_size(int32_t L, int32_t E, int32_t n_ranked);
+moe_status moe_strp_write(const uint16_t* pairs, int32_t n_ranked, int32_t L, int32_t E, void* out,
+                          size_t out_bytes);
+moe_status moe_strp_read(const void* buf, size_t bytes, int32_t* L, int32_t* E, int32_t* n_ranked,
+                         uint16_t* pairs, int32_t pairs_capacity, int16_t* inverse, int64_t inverse_capacity);
+moe_status moe_profile_remap(const uint16_t* pairs, int32_t n, int32_t L, int32_t E_old, const int32_t* keep_map,
+                             int32_t keep, uint16_t* out, int32_t* n_out);
+
 #ifdef __cplusplus
 }
 #endif

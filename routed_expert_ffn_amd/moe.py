@@ -18,7 +18,8 @@ F32, BF16, INT4_B32 = 0, 1, 2
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_ffn_workspace_size", "moe_ffn",
-           "moe_combine", "moe_expert_freq"]
+           "moe_combine", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
+           "moe_profile_hits", "moe_strp_size", "moe_strp_write", "moe_strp_read", "moe_profile_remap"]
 
 
 class MoeError(RuntimeError):
@@ -71,6 +72,20 @@ def load():
     L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp]
     L.moe_expert_freq.restype = ctypes.c_int
     L.moe_expert_freq.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, vp, vp, vp]
+    L.moe_profile_workspace_size.restype = sz
+    L.moe_profile_workspace_size.argtypes = [i32, i32]
+    L.moe_profile_rank.restype = ctypes.c_int
+    L.moe_profile_rank.argtypes = [vp, i32, i32, vp, vp, vp, sz, vp]
+    L.moe_profile_hits.restype = ctypes.c_int
+    L.moe_profile_hits.argtypes = [vp, i32, i64, i32, vp, i32, i64, vp, vp]
+    L.moe_strp_size.restype = sz
+    L.moe_strp_size.argtypes = [i32, i32, i32]
+    L.moe_strp_write.restype = ctypes.c_int
+    L.moe_strp_write.argtypes = [vp, i32, i32, i32, vp, sz]
+    L.moe_strp_read.restype = ctypes.c_int
+    L.moe_strp_read.argtypes = [vp, sz, vp, vp, vp, vp, i32, vp, i64]
+    L.moe_profile_remap.restype = ctypes.c_int
+    L.moe_profile_remap.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp]
     _lib = L
     return L
 
@@ -260,6 +275,75 @@ def expert_freq(logits, K: int, keep: int = 0, counts=None, accumulate: bool = F
     _chk(load().moe_expert_freq(_ptr(logits), L, T, E, K, _ptr(counts), 1 if accumulate else 0, keep, _ptr(rank_of),
                                 _ptr(keep_map), _stream(stream)), "moe_expert_freq")
     return counts, rank_of, keep_map
+
+
+# ------------------------------------------------------------------ expert profile
+def profile_rank(counts, workspace=None, stream=None):
+    """counts [L][E] int64 (device) -> (rank [L][E] int32, pairs [L*E][2] int16 holding uint16 (layer, expert))."""
+    _need(counts, "counts", torch.int64)
+    L, E = counts.shape
+    dev = counts.device
+    rank = torch.empty((L, E), dtype=torch.int32, device=dev)
+    pairs = torch.empty((L * E, 2), dtype=torch.int16, device=dev)
+    nb = int(load().moe_profile_workspace_size(L, E))
+    ws = _workspace(nb, dev, workspace)
+    _chk(load().moe_profile_rank(_ptr(counts), L, E, _ptr(rank), _ptr(pairs), _ptr(ws), nb, _stream(stream)),
+         "moe_profile_rank")
+    return rank, pairs
+
+
+def profile_hits(trace, rank, S: int, stream=None):
+    """trace [L][T][K] int32, rank [L][E] int32 (device) -> hits (a 1-element int64 tensor, device)."""
+    _need(trace, "trace", torch.int32)
+    _need(rank, "rank", torch.int32)
+    L, T, K = trace.shape
+    E = rank.shape[1]
+    hits = torch.empty(1, dtype=torch.int64, device=trace.device)   # the uint64 count, < 2^63
+    _chk(load().moe_profile_hits(_ptr(trace), L, T, K, _ptr(rank), E, int(S), _ptr(hits), _stream(stream)),
+         "moe_profile_hits")
+    return hits
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def strp_write(pairs, L: int, E: int) -> bytes:
+    """Host pairs [n][2] (uint16 (layer, expert) in rank order) -> the STRP v1 file's bytes."""
+    import numpy as np
+    p = np.ascontiguousarray(np.asarray(pairs, dtype=np.uint16).reshape(-1, 2))
+    n = p.shape[0]
+    nb = int(load().moe_strp_size(L, E, n))
+    out = np.empty(nb, dtype=np.uint8)
+    _chk(load().moe_strp_write(_np_ptr(p), n, L, E, _np_ptr(out), nb), "moe_strp_write")
+    return out.tobytes()
+
+
+def strp_read(buf: bytes):
+    """STRP v1 bytes -> (L, E, pairs [n][2] uint16, inverse [L][E] int16)."""
+    import numpy as np
+    b = np.frombuffer(buf, dtype=np.uint8).copy()
+    L, E, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _chk(load().moe_strp_read(_np_ptr(b), b.size, ctypes.byref(L), ctypes.byref(E), ctypes.byref(n), None, 0, None,
+                              0), "moe_strp_read")
+    pairs = np.empty((n.value, 2), dtype=np.uint16)
+    inv = np.empty((L.value, E.value), dtype=np.int16)
+    _chk(load().moe_strp_read(_np_ptr(b), b.size, ctypes.byref(L), ctypes.byref(E), ctypes.byref(n), _np_ptr(pairs),
+                              n.value, _np_ptr(inv), inv.size), "moe_strp_read")
+    return L.value, E.value, pairs, inv
+
+
+def profile_remap(pairs, keep_map, E_old: int):
+    """Host ranked pairs of an E_old-expert profile + keep_map [L][keep] -> the pruned model's ranked pairs."""
+    import numpy as np
+    p = np.ascontiguousarray(np.asarray(pairs, dtype=np.uint16).reshape(-1, 2))
+    km = np.ascontiguousarray(np.asarray(keep_map, dtype=np.int32))
+    L, keep = km.shape
+    out = np.empty((max(p.shape[0], 1), 2), dtype=np.uint16)
+    m = ctypes.c_int32()
+    _chk(load().moe_profile_remap(_np_ptr(p), p.shape[0], L, E_old, _np_ptr(km), keep, _np_ptr(out),
+                                  ctypes.byref(m)), "moe_profile_remap")
+    return out[:m.value].copy()
 
 
 # ------------------------------------------------------------------ one whole layer

@@ -360,3 +360,44 @@ def test_freq_full_size_two_layers_and_invariants():
     assert np.array_equal(to_host(c), ref_c)
     assert np.array_equal(to_host(rk), ref_r) and np.array_equal(to_host(km), ref_k)
     assert np.all(to_host(c).sum(axis=1) == T * K)
+
+
+# ---------------------------------------------------------------- expert profile (global ranking, hit rate)
+def test_profile_rank_matches_oracle():
+    """Global (layer, expert) ranking on the GPU, bit-exact against the oracle:
+    small counts (many ties across and within layers), a ragged shape, the
+    statistic's 48 x 512, and a single wide layer."""
+    from oracle import profile as P
+    rng = np.random.default_rng(11)
+    cases = [rng.integers(0, 3, size=(7, 300)), rng.integers(0, 50, size=(48, 512)),
+             (rng.zipf(1.3, size=(48, 512)) % 100000).astype(np.int64), rng.integers(0, 5, size=(1, 4096)),
+             np.zeros((3, 5), dtype=np.int64)]
+    for counts in cases:
+        rank, pairs = moe.profile_rank(torch.from_numpy(np.ascontiguousarray(counts, dtype=np.int64)).cuda())
+        torch.cuda.synchronize()
+        ref_pairs, ref_rank = P.global_rank(counts)
+        assert np.array_equal(to_host(rank), ref_rank)
+        assert np.array_equal(to_host(pairs).view(np.uint16), ref_pairs)
+
+
+def test_profile_hits_match_oracle():
+    """Reads of a routing trace that land on the first S ranked pairs, against
+    the oracle, for a profile built from the trace itself and a random one."""
+    from oracle import profile as P
+    rng = np.random.default_rng(12)
+    L, T, K, E = 4, 3000, 10, 256
+    bias = -1.1 * np.log1p(rng.permutation(E))
+    trace = np.stack([np.argsort(-(rng.standard_normal((T, E)) + bias), axis=1)[:, :K] for _ in range(L)])
+    trace = trace.astype(np.int32)
+    counts = np.stack([np.bincount(trace[l].reshape(-1), minlength=E) for l in range(L)]).astype(np.int64)
+    perm = rng.permutation(L * E)
+    rand_counts = np.empty(L * E, dtype=np.int64)
+    rand_counts[perm] = np.arange(L * E)[::-1]
+    td = torch.from_numpy(trace).cuda()
+    for cnt in (counts, rand_counts.reshape(L, E)):
+        rank, pairs = moe.profile_rank(torch.from_numpy(cnt).cuda())
+        ref_pairs, _ = P.global_rank(cnt)
+        for S in (0, 1, 100, 257, L * E):
+            h = moe.profile_hits(td, rank, S)
+            torch.cuda.synchronize()
+            assert int(h.cpu().item()) == P.hits(trace, ref_pairs, S)[0]
