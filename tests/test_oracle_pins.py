@@ -532,3 +532,33 @@ def test_profile_hit_rate_closed_forms():
         rp = np.stack([perm // E, perm % E], axis=1).astype(np.uint16)
         acc.append(P.hits(trace, rp, S)[0] / (L * T * K))
     assert abs(np.mean(acc) - S / (L * E)) < 0.01
+
+
+# ------------------------------------------------------------------ steered combine
+def test_steer_projection_closed_forms():
+    """h - (h.v) v for a unit v: orthogonal to v, idempotent, no change for v
+    orthogonal to h, the j-th coordinate zeroed for v = e_j, the same for -v,
+    never longer than h; the combine part is a plain weighted gather."""
+    from oracle import steer as St
+    rng = np.random.default_rng(9)
+    T, H = 6, 96
+    h = rng.standard_normal((T, H))
+    v = rng.standard_normal(H)
+    v /= np.linalg.norm(v)
+    p = St.project_out(h, v)
+    assert np.max(np.abs(p @ v)) < 1e-12 * np.max(np.abs(h))
+    assert np.allclose(St.project_out(p, v), p, rtol=0, atol=1e-13)
+    assert np.array_equal(St.project_out(h, -v), p) or np.allclose(St.project_out(h, -v), p, rtol=0, atol=1e-14)
+    assert np.all(np.linalg.norm(p, axis=1) <= np.linalg.norm(h, axis=1) + 1e-12)
+    e = np.zeros(H); e[7] = 1.0
+    pe = St.project_out(h, e)
+    assert np.all(pe[:, 7] == 0) and np.array_equal(np.delete(pe, 7, axis=1), np.delete(h, 7, axis=1))
+    u = np.zeros(H); u[3] = 1.0
+    hz = h.copy(); hz[:, 3] = 0.0
+    assert np.array_equal(St.project_out(hz, u), hz)
+    # combine: two tokens, K = 2, hand-worked
+    y = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [7.0, 8.0]])
+    inv = np.array([2, 0, 1, 3])
+    w = np.array([[0.5, 0.25], [1.0, -1.0]])
+    res = np.array([[0.0, 1.0], [2.0, 0.0]])
+    assert St.combine_rows(y, inv, w, res).tolist() == [[2.75, 4.5], [-2.0, -4.0]]
