@@ -180,20 +180,27 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
         for p in per_set:
             moe.combine(y, p["inv"], p["w"], out=lw.out)
 
+    v = torch.from_numpy(synth.steer_vector(shape.H)).to(dev)
+
+    def calls_combine_steer():
+        for p in per_set:
+            moe.combine(y, p["inv"], p["w"], out=lw.out, steer_v=v)
+
     parts = {}
     for pname, f in (("route", calls_route), ("permute", calls_permute), ("ffn", calls_ffn),
-                     ("combine", calls_combine)):
+                     ("combine", calls_combine), ("combine_steer", calls_combine_steer)):
         gf = capture(torch, f).replay if use_graph else f
         timer.run(gf, wreps)
         t, _ = timer.run(gf, reps)
         parts[pname] = t / n_steps * 1e6
+    steer_us = parts.pop("combine_steer")
     b_step = sum(a["b_step"] for a in acct) / len(acct)
     b_ffn = sum(a["b_ffn"] for a in acct) / len(acct)
     f_ffn = acct[0]["f_ffn"]
     f_all = acct[0]["f_ffn"] + acct[0]["f_router"]
     touched = sum(a["touched"] for a in acct) / len(acct)
     res = dict(name=name, T=shape.T, ms_per_step=ms, value=shape.T / (ms / 1e3), steps=n_steps, warmup=wreps * sets,
-               wall_s=wall, parts_us=parts, touched_experts=touched, bytes_per_step=b_step, bytes_ffn=b_ffn,
+               wall_s=wall, parts_us=parts, combine_steer_us=steer_us, touched_experts=touched, bytes_per_step=b_step, bytes_ffn=b_ffn,
                flops_ffn=f_ffn, flops_step=f_all,
                hbm_frac_step=b_step / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
                mfma_frac_step=f_all / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
@@ -302,27 +309,37 @@ def bench_copy(torch, steps):
 
 
 # ------------------------------------------------------------------ pruned 48-layer int4 stack
-def bench_stack(torch, moe, synth, shape, steps, warmup, use_graph, name):
+def bench_stack(torch, moe, synth, shape, steps, warmup, use_graph, name, steered=41):
+    """The 48-layer int4 stack, each layer's output added to the stream in
+    place; timed plain and with the first `steered` layers steered (the pages
+    steer 41 layers without naming them)."""
     Ls = synth.STACK_INT4_LAYERS
     log(f"[{name}] generating {Ls} int4 layers")
     layers = [synth.make_device_layer(shape, seed=0, cfg=5, layer=l, device="cuda") for l in range(Ls)]
+    vs = [torch.from_numpy(synth.steer_vector(shape.H, layer=l)).cuda() if l < steered else None for l in range(Ls)]
     x0 = layers[0].x
     torch.cuda.synchronize()
     lw = moe.LayerWorkspace(shape.T, shape.H, shape.E, shape.K, shape.F, x_dtype=torch.bfloat16, w_dtype=moe.INT4_B32)
     h = torch.empty_like(x0)
 
-    def step():
-        h.copy_(x0)
-        for L in layers:
-            moe.layer(h, L.wr, L.wg, L.wu, L.wd, shape.K, sg=L.sg, su=L.su, sd=L.sd, residual=h, lw=lw, out=h)
-    timer = Timer(torch)
-    fn = capture(torch, step).replay if use_graph else step
-    timer.run(fn, max(1, warmup))
-    n = max(2, steps)
-    dt, wall = timer.run(fn, n)
-    ms = dt / n * 1e3
+    def run(steer):
+        def step():
+            h.copy_(x0)
+            for L, v in zip(layers, vs):
+                moe.layer(h, L.wr, L.wg, L.wu, L.wd, shape.K, sg=L.sg, su=L.su, sd=L.sd, residual=h, lw=lw, out=h,
+                          steer_v=v if steer else None)
+        timer = Timer(torch)
+        fn = capture(torch, step).replay if use_graph else step
+        timer.run(fn, max(1, warmup))
+        n = max(2, steps)
+        dt, wall = timer.run(fn, n)
+        return dt / n * 1e3, n, wall
+
+    ms, n, wall = run(False)
+    ms_s, _, _ = run(True)
     res = dict(name=name, T=shape.T, layers=Ls, ms_per_step=ms, ms_per_layer=ms / Ls,
-               value=shape.T * Ls / (ms / 1e3), unit="tokens/s per MoE layer (48-layer stack)", steps=n, wall_s=wall)
+               value=shape.T * Ls / (ms / 1e3), unit="tokens/s per MoE layer (48-layer stack)", steps=n, wall_s=wall,
+               steered_layers=steered, ms_per_step_steered=ms_s, steer_cost_frac=ms_s / ms - 1.0)
     del layers
     return res
 
@@ -377,13 +394,15 @@ def main():
         main_res = bench_layer(torch, moe, synth, synth.VERIFY_BF16, 2, args.steps, args.warmup, N_SETS, use_graph,
                                "verify step 5 tok, E512 top-10 bf16")
         main_res["is_verify_layer"] = True
-        log(f"[verify] {main_res['ms_per_step']*1e3:.1f} us/step  parts {main_res['parts_us']}")
+        log(f"[verify] {main_res['ms_per_step']*1e3:.1f} us/step  parts {main_res['parts_us']}  "
+            f"steered combine {main_res['combine_steer_us']:.2f} us")
     if "prefill" in wl:
         r = bench_layer(torch, moe, synth, synth.PREFILL_BF16, 3, max(8, args.steps // 10), 8, 1, use_graph,
                         "prefill chunk 8192 tok, E512 top-10 bf16, Zipf(1.1) router offset")
         r["roofline"] = roofline_for(r, "mfma", "ffn_prefill")
         r["unit"] = "tokens/s"
-        log(f"[prefill] {r['ms_per_step']:.3f} ms/step  parts {r['parts_us']}")
+        log(f"[prefill] {r['ms_per_step']:.3f} ms/step  parts {r['parts_us']}  "
+            f"steered combine {r['combine_steer_us']:.2f} us")
         also.append(r)
         torch.cuda.empty_cache()
     if "freq" in wl:
@@ -401,7 +420,7 @@ def main():
         for shp, nm in ((synth.STACK_INT4_VERIFY, "pruned 48-layer int4 stack, 5-tok verify"),
                         (synth.STACK_INT4_PREFILL, "pruned 48-layer int4 stack, 8192-tok prefill")):
             r = bench_stack(torch, moe, synth, shp, max(3, args.steps // 40), 1, use_graph, nm)
-            log(f"[stack T={shp.T}] {r['ms_per_step']:.3f} ms/step")
+            log(f"[stack T={shp.T}] {r['ms_per_step']:.3f} ms/step, {r['ms_per_step_steered']:.3f} ms steered")
             also.append(r)
             torch.cuda.empty_cache()
 

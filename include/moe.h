@@ -159,6 +159,23 @@ moe_status moe_combine(const void* y_perm, int32_t y_dtype, const int32_t* inv_p
                        int32_t T, int32_t K, int32_t H, void* out, int32_t out_dtype,
                        moe_stream stream);
 
+/* ---------------------------------------------------------------- steered combine
+ * moe_combine followed by the steering projection of a steered layer (the
+ * kwkr.cn Coder write-up, "实验加速投影在 Coder 上的表现": one unit direction
+ * per steered layer, whose component is removed from the stream after it):
+ *     h[t]   = sum_k topk_w[t][k] * y_perm[inv_perm[t*K+k]] + residual[t]
+ *     out[t] = cast( h[t] - (h[t] . v) v )
+ * h, the dot product and the subtraction in fp32 (the dot summed in a fixed
+ * order: the result does not vary from run to run), one rounding at the end.
+ *   steer_v  [H] fp32, device, 16-byte aligned; used as given (the caller
+ *            passes a unit vector; it is not renormalised here).
+ * Other arguments, aliasing and dtypes as for moe_combine; layers that are
+ * not steered call moe_combine.  Unsupported: H > 8192 or not a multiple of 8. */
+moe_status moe_combine_steer(const void* y_perm, int32_t y_dtype, const int32_t* inv_perm,
+                             const float* topk_w, const void* residual, const float* steer_v,
+                             int32_t T, int32_t K, int32_t H, void* out, int32_t out_dtype,
+                             moe_stream stream);
+
 /* ---------------------------------------------------------------- pruning statistic
  * Per-(layer, expert) selection counts over given router logits (page 1 §3:
  * routing counted on calibration data, the most-selected kept per layer, kept

@@ -168,6 +168,20 @@ moe_status moe_combine(const void* y_perm, int32_t y_dtype, const int32_t* inv_p
                                      out_dtype == MOE_BF16, S(stream)));
 }
 
+moe_status moe_combine_steer(const void* y_perm, int32_t y_dtype, const int32_t* inv_perm, const float* topk_w,
+                             const void* residual, const float* steer_v, int32_t T, int32_t K, int32_t H, void* out,
+                             int32_t out_dtype, moe_stream stream) {
+    if (T < 0 || K <= 0 || H <= 0 || (int64_t)T * K > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (!steer_v || (T > 0 && (!y_perm || !inv_perm || !topk_w || !out))) return MOE_ERR_INVALID_ARG;
+    if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+        return MOE_ERR_INVALID_ARG;
+    if (H % 8 != 0 || H > STEER_MAX_H || !aligned16(y_perm) || !aligned16(residual) || !aligned16(out) ||
+        !aligned16(steer_v))
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_combine_steer(y_perm, y_dtype == MOE_BF16, inv_perm, topk_w, residual, steer_v, T, K, H,
+                                           out, out_dtype == MOE_BF16, S(stream)));
+}
+
 moe_status moe_expert_freq(const float* logits, int32_t L, int64_t T, int32_t E, int32_t K, int64_t* counts,
                            int32_t accumulate, int32_t keep, int32_t* rank_of, int32_t* keep_map,
                            moe_stream stream) {

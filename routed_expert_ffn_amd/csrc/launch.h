@@ -64,6 +64,9 @@ hipError_t launch_ffn_gemm(const void* x, const void* wg, const void* wu, const 
 // combine.hip
 hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w, const void* res, int T,
                           int K, int H, void* out, int out_bf16, hipStream_t st);
+constexpr int STEER_MAX_H = 8192;   // the steered combine keeps one token row per block in registers
+hipError_t launch_combine_steer(const void* y, int y_bf16, const int32_t* inv, const float* w, const void* res,
+                                const float* sv, int T, int K, int H, void* out, int out_bf16, hipStream_t st);
 
 // freq.hip
 hipError_t launch_freq(const float* logits, int L, int64_t T, int E, int K, unsigned long long* counts,

@@ -18,7 +18,7 @@ F32, BF16, INT4_B32 = 0, 1, 2
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_ffn_workspace_size", "moe_ffn",
-           "moe_combine", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
+           "moe_combine", "moe_combine_steer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
            "moe_profile_hits", "moe_strp_size", "moe_strp_write", "moe_strp_read", "moe_profile_remap"]
 
 
@@ -70,6 +70,8 @@ def load():
                           vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp]
+    L.moe_combine_steer.restype = ctypes.c_int
+    L.moe_combine_steer.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp]
     L.moe_expert_freq.restype = ctypes.c_int
     L.moe_expert_freq.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, vp, vp, vp]
     L.moe_profile_workspace_size.restype = sz
@@ -241,8 +243,10 @@ def ffn(x, wg, wu, wd, offsets, perm, K: int, sg=None, su=None, sd=None, y_dtype
 
 
 # ------------------------------------------------------------------ moe_combine
-def combine(y_perm, inv_perm, topk_w, residual=None, out_dtype=None, out=None, stream=None):
-    """out [T][H] = sum_k w * y_perm[inv] (+ residual)."""
+def combine(y_perm, inv_perm, topk_w, residual=None, out_dtype=None, out=None, stream=None, steer_v=None):
+    """out [T][H] = sum_k w * y_perm[inv] (+ residual); with steer_v ([H] fp32
+    unit vector) the row's component along it is removed before rounding
+    (moe_combine_steer)."""
     _need(y_perm, "y_perm")
     _need(topk_w, "topk_w", torch.float32)
     T, K = topk_w.shape
@@ -254,6 +258,12 @@ def combine(y_perm, inv_perm, topk_w, residual=None, out_dtype=None, out=None, s
         _need(residual, "residual", out_dtype, (T, H))
     o = out if out is not None else torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
     _need(o, "out", out_dtype, (T, H))
+    if steer_v is not None:
+        _need(steer_v, "steer_v", torch.float32, (H,))
+        _chk(load().moe_combine_steer(_ptr(y_perm), _act_dtype(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(residual),
+                                      _ptr(steer_v), T, K, H, _ptr(o), _act_dtype(o), _stream(stream)),
+             "moe_combine_steer")
+        return o
     _chk(load().moe_combine(_ptr(y_perm), _act_dtype(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(residual), T, K, H,
                             _ptr(o), _act_dtype(o), _stream(stream)), "moe_combine")
     return o
@@ -365,8 +375,9 @@ class LayerWorkspace:
 
 
 def layer(x, w_router, wg, wu, wd, K: int, bias=None, sg=None, su=None, sd=None, residual=None, lw=None,
-          stream=None, out=None):
-    """route -> permute -> ffn -> combine for one MoE layer.  Returns (out, routing dict)."""
+          stream=None, out=None, steer_v=None):
+    """route -> permute -> ffn -> combine (steered if steer_v is given) for one
+    MoE layer.  Returns (out, routing dict)."""
     T, H = x.shape
     E, F = wg.shape[0], wg.shape[1]
     idx, w = route(x, w_router, K, bias=bias, workspace=lw.route_ws if lw else None, stream=stream,
@@ -377,5 +388,5 @@ def layer(x, w_router, wg, wu, wd, K: int, bias=None, sg=None, su=None, sd=None,
             out=lw.y if lw else None, workspace=lw.ffn_ws if lw else None, stream=stream)
     if out is None and lw is not None:
         out = lw.out
-    o = combine(y, inv, w, residual=residual, out_dtype=x.dtype, out=out, stream=stream)
+    o = combine(y, inv, w, residual=residual, out_dtype=x.dtype, out=out, stream=stream, steer_v=steer_v)
     return o, dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, y=y)

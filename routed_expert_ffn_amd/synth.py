@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for seed derivation
-TID_X, TID_WR, TID_PERM, TID_WG, TID_WU, TID_WD, TID_Z = 0, 1, 2, 3, 4, 5, 6
+TID_X, TID_WR, TID_PERM, TID_WG, TID_WU, TID_WD, TID_Z, TID_V = 0, 1, 2, 3, 4, 5, 6, 7
 
 ZIPF_S = 1.1
 INT4_BLOCK = 32
@@ -149,6 +149,14 @@ def make_host_layer(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0,
         out.wu, out.su = int4_quantize(wu)
         out.wd, out.sd = int4_quantize(wd)
     return out
+
+
+def steer_vector(H: int, seed: int = 0, cfg: int = 5, layer: int = 0) -> np.ndarray:
+    """A synthetic steering direction: [H] fp32, N(0,1) entries scaled (in fp64)
+    to unit length.  The pages' vectors come from a trained model; only their
+    shape (one unit direction per steered layer) is reproduced."""
+    v = np_rng(seed, cfg, layer, TID_V).standard_normal(H)
+    return (v / np.linalg.norm(v)).astype(np.float32)
 
 
 def make_host_logits(L: int, T: int, E: int, seed: int = 0, cfg: int = 3, zipf: bool = True,

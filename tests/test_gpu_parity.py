@@ -246,6 +246,87 @@ def test_combine_in_place_residual_and_fp32():
     assert torch.equal(out, res2)
 
 
+# ---------------------------------------------------------------- steered combine
+@pytest.mark.parametrize("ydt,odt,T,K,H,with_res", [
+    ("f32", "f32", 37, 4, 256, True),        # one partial chunk
+    ("bf16", "bf16", 5, 10, 2048, True),      # the verify step's shape
+    ("bf16", "f32", 19, 10, 2560, False),     # two chunks, the second ragged (the pages' stream width)
+    ("bf16", "bf16", 3, 8, 8192, True),       # the widest row one block holds
+    ("f32", "bf16", 0, 4, 256, True),         # no tokens
+])
+def test_combine_steer_matches_oracle(ydt, odt, T, K, H, with_res):
+    from oracle import steer
+    rng = np.random.default_rng(T * 131 + H)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    y = torch.from_numpy(rng.standard_normal((T * K, H)).astype(np.float32)).to(tdt[ydt]).cuda()
+    inv = torch.from_numpy(rng.permutation(T * K).astype(np.int32)).cuda()
+    w = torch.from_numpy(rng.random((T, K)).astype(np.float32)).cuda()
+    res = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(tdt[odt]).cuda() if with_res else None
+    v = torch.from_numpy(synth.steer_vector(H, seed=T, layer=H)).cuda()
+    out = moe.combine(y, inv, w, residual=res, out_dtype=tdt[odt], steer_v=v)
+    again = moe.combine(y, inv, w, residual=res, out_dtype=tdt[odt], steer_v=v)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "the steered combine must not vary from run to run"
+    if T == 0:
+        return
+    ref = steer.combine_steer(as_f64(to_host(y)), to_host(inv), to_host(w), to_host(v).astype(np.float64),
+                              None if res is None else as_f64(to_host(res)))
+    got = as_f64(to_host(out))
+    assert row_rel_err(got, ref) <= (TOL_F32 if odt == "f32" else TOL_BF16)
+    # what is left along v is the output's own rounding: with fp32 output a
+    # few units of fp32 precision of the row, with bf16 a few of bf16
+    along = np.abs(got @ to_host(v).astype(np.float64)) / np.linalg.norm(got, axis=1)
+    assert along.max() <= (1e-5 if odt == "f32" else 2e-2)
+
+
+def test_combine_steer_in_place_and_unit_axis():
+    """out aliasing residual gives the same bytes; v = e_j zeroes column j exactly
+    and leaves every other column as the plain combine rounds it."""
+    rng = np.random.default_rng(77)
+    T, K, H = 29, 6, 2560
+    y = torch.from_numpy(rng.standard_normal((T * K, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    inv = torch.from_numpy(rng.permutation(T * K).astype(np.int32)).cuda()
+    w = torch.from_numpy(rng.random((T, K)).astype(np.float32)).cuda()
+    res = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(synth.steer_vector(H, seed=3)).cuda()
+    out = moe.combine(y, inv, w, residual=res, steer_v=v)
+    res2 = res.clone()
+    moe.combine(y, inv, w, residual=res2, out=res2, steer_v=v)
+    e = torch.zeros(H, dtype=torch.float32, device="cuda")
+    e[2049] = 1.0
+    unit = moe.combine(y, inv, w, residual=res, steer_v=e)
+    plain = moe.combine(y, inv, w, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(out, res2)
+    assert torch.all(unit[:, 2049] == 0)
+    keep = torch.ones(H, dtype=torch.bool, device="cuda")
+    keep[2049] = False
+    assert torch.equal(unit[:, keep], plain[:, keep])
+
+
+def test_steered_int4_verify_layer_full_size():
+    """One steered layer of the pruned int4 stack at the verify shape, updating
+    the stream in place: routing exact, output within the bf16 bound of the
+    oracle's fp64 combine + residual + projection."""
+    from oracle import steer
+    s = synth.STACK_INT4_VERIFY
+    d = synth.make_device_layer(s, seed=0, cfg=5, layer=1, device="cuda")
+    v = torch.from_numpy(synth.steer_vector(s.H, layer=1)).cuda()
+    torch.cuda.synchronize()
+    x, wr = to_host(d.x), to_host(d.wr)
+    ref_idx, ref_w, _ = oracle.route(x, wr, s.K)
+    lw = moe.LayerWorkspace(s.T, s.H, s.E, s.K, s.F, x_dtype=d.x.dtype, w_dtype=moe.INT4_B32)
+    h = d.x.clone()
+    out, r = moe.layer(h, d.wr, d.wg, d.wu, d.wd, s.K, sg=d.sg, su=d.su, sd=d.sd, residual=h, lw=lw, out=h,
+                       steer_v=v)
+    torch.cuda.synchronize()
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    _, yk = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d), want_y=True)
+    hh = (ref_w.astype(np.float64)[:, :, None] * yk).sum(axis=1) + as_f64(x)
+    ref = steer.project_out(hh, to_host(v).astype(np.float64))
+    assert row_rel_err(to_host(out), ref) <= TOL_BF16
+
+
 # ---------------------------------------------------------------- decode/verify step, full size
 def test_verify_step_full_size():
     s = synth.VERIFY_BF16
