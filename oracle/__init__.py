@@ -19,8 +19,8 @@ LIB = os.path.join(BUILD_DIR, "liboracle.so")
 # a deliberately mutated oracle build (planted-mistake tests) may be loaded instead
 _LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB_OVERRIDE")
 
-F32, BF16, INT4 = 0, 1, 2
-_DT = {"f32": F32, "bf16": BF16, "int4": INT4}
+F32, BF16, INT4, INT2, INT3 = 0, 1, 2, 3, 4
+_DT = {"f32": F32, "bf16": BF16, "int4": INT4, "int2": INT2, "int3": INT3}
 
 
 def build(force: bool = True) -> str:
@@ -56,6 +56,7 @@ def lib():
         L.oracle_fp16_value.restype = ctypes.c_double
         L.oracle_fp16_value.argtypes = [ctypes.c_uint16]
         L.oracle_int4_dequant.argtypes = [vp, vp, i64, i64, vp]
+        L.oracle_lowbit_dequant.argtypes = [vp, vp, i64, i64, i32, vp]
         L.oracle_router_logits.argtypes = [vp, i32, vp, vp, i64, i32, i32, vp]
         L.oracle_topk.argtypes = [vp, i64, i32, i32, vp, vp]
         L.oracle_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
@@ -111,6 +112,17 @@ def int4_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
+def lowbit_dequant(packed: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
+    """Dequantise a 2-D int2 (bits 2) or int3 (bits 3) matrix [rows][cols*bits/8]
+    with fp16 scales [rows][cols/32] (R16)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales).view(np.uint16)
+    rows, cols = packed.shape[0], packed.shape[1] * 8 // bits
+    out = np.empty((rows, cols), dtype=np.float64)
+    _check(lib().oracle_lowbit_dequant(_p(packed), _p(sc), rows, cols, bits, _p(out)), "lowbit_dequant")
+    return out
+
+
 # ---------------------------------------------------------------- a1 / a2
 def router_logits(x, wr, bias=None) -> np.ndarray:
     x, xdt = _act(x)
@@ -154,7 +166,7 @@ def permute(idx, E: int):
 
 # ---------------------------------------------------------------- a4 / a5
 class Weights:
-    """Expert weights as host arrays: f32, bf16 bits (uint16) or int4 (packed + fp16 scales)."""
+    """Expert weights as host arrays: f32, bf16 bits (uint16) or int4 / int3 / int2 (packed + fp16 scales)."""
 
     def __init__(self, wdt, wg, wu, wd, sg=None, su=None, sd=None):
         self.dt = _DT[wdt]

@@ -41,6 +41,12 @@
  *       in fp64 in k order and one final rounding (fp32, or bf16 RNE).
  *   R7  int4: w = d * (nibble - 8), d the fp16 scale of the 32-element block
  *       along the input dimension; byte j holds element 2j low, 2j+1 high.
+ *   R16 int2 / int3 (a lower-bit expert variant): w = d * (u - 2) or d * (u - 4),
+ *       u the element's stored level, d the fp16 scale of its 32-element block.
+ *       A row holds the low two bits of every level as 32-bit little-endian
+ *       words of 16 elements (element 4k + j of a word in byte j, bits 2k and
+ *       2k + 1); int3 rows then hold the third bit as words of 32 elements
+ *       (element 16g + 4k + j of a word in byte j, bit 4g + k).
  *   R8  counts[l][e] = number of rows whose top-K holds e; rank by (count
  *       descending, index ascending); keep_map[l] = the ids of rank < keep,
  *       in ascending id order.
@@ -52,7 +58,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_INT4 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_INT4 = 2, OR_INT2 = 3, OR_INT3 = 4 };
 enum { OR_OK = 0, OR_EINVAL = 1, OR_ENAN = 2, OR_ENOMEM = 3 };
 
 int oracle_rank_keep(const int64_t* counts, int L, int E, int keep, int32_t* rank_of, int32_t* keep_map);
@@ -104,17 +110,50 @@ static double act_value(const void* x, int dt, int64_t i) {
     return dt == OR_F32 ? (double)((const float*)x)[i] : oracle_bf16_value(((const uint16_t*)x)[i]);
 }
 
+/* The stored level u of element c of one int2 or int3 row of `cols`
+ * elements (R16). */
+static int lowbit_level(const uint8_t* row, int64_t cols, int bits, int64_t c) {
+    const int64_t word = c / 16;
+    const int i = (int)(c % 16), k = i / 4, j = i % 4;
+    int u = (row[word * 4 + j] >> (2 * k)) & 3;
+    if (bits == 3) {
+        const uint8_t* third = row + cols / 4;
+        const int64_t word3 = c / 32;
+        const int i3 = (int)(c % 32), g = i3 / 16, k3 = (i3 % 16) / 4, j3 = i3 % 4;
+        u |= ((third[word3 * 4 + j3] >> (4 * g + k3)) & 1) << 2;
+    }
+    return u;
+}
+
 /* One weight element of matrix `mat` (shape [E][rows][cols], out x in) at
- * (e, r, c), as an exact double.  R7 for int4. */
+ * (e, r, c), as an exact double.  R7 for int4, R16 for int2 / int3. */
 static double weight_value(const void* mat, const uint16_t* scales, int dt,
                            int64_t e, int64_t rows, int64_t cols, int64_t r, int64_t c) {
     int64_t flat = (e * rows + r) * cols + c;
     if (dt == OR_F32) return (double)((const float*)mat)[flat];
     if (dt == OR_BF16) return oracle_bf16_value(((const uint16_t*)mat)[flat]);
-    uint8_t byte = ((const uint8_t*)mat)[flat / 2];
-    int q = ((c & 1) ? (byte >> 4) : (byte & 15)) - 8;
     double d = oracle_fp16_value(scales[(e * rows + r) * (cols / 32) + c / 32]);
+    int q;
+    if (dt == OR_INT4) {
+        uint8_t byte = ((const uint8_t*)mat)[flat / 2];
+        q = ((c & 1) ? (byte >> 4) : (byte & 15)) - 8;
+    } else {
+        const int bits = dt == OR_INT2 ? 2 : 3;
+        const int64_t row_bytes = cols * bits / 8;
+        q = lowbit_level((const uint8_t*)mat + (e * rows + r) * row_bytes, cols, bits, c) - (1 << (bits - 1));
+    }
     return d * (double)q;
+}
+
+/* Dequantise an int2 (bits = 2) or int3 (bits = 3) matrix [rows][cols] to
+ * doubles (used by the format pins). */
+int oracle_lowbit_dequant(const uint8_t* packed, const uint16_t* scales, int64_t rows, int64_t cols, int bits,
+                          double* out) {
+    if (cols % 32 || (bits != 2 && bits != 3)) return OR_EINVAL;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            out[r * cols + c] = weight_value(packed, scales, bits == 2 ? OR_INT2 : OR_INT3, 0, rows, cols, r, c);
+    return OR_OK;
 }
 
 /* Dequantise one int4 matrix row range to doubles (used by the format pin). */
@@ -270,7 +309,8 @@ int oracle_layer_rows(const void* x, int x_dt, const int32_t* idx, const float* 
                       int H, int F, const void* res, const int64_t* rows, int64_t n_rows,
                       int out_dt, void* out_rows, double* y_rows) {
     if (!x || !idx || !w || !wg || !wu || !wd || !rows || !out_rows || H <= 0 || F <= 0) return OR_EINVAL;
-    if (w_dt == OR_INT4 && (!sg || !su || !sd || H % 32 || F % 32)) return OR_EINVAL;
+    if (w_dt >= OR_INT4 && (!sg || !su || !sd || H % 32 || F % 32)) return OR_EINVAL;
+    if (w_dt < OR_F32 || w_dt > OR_INT3) return OR_EINVAL;
     double* y = (double*)malloc(sizeof(double) * (size_t)H);
     double* acc = (double*)malloc(sizeof(double) * (size_t)H);
     if (!y || !acc) { free(y); free(acc); return OR_ENOMEM; }

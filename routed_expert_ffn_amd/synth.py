@@ -41,7 +41,7 @@ class LayerShape:
     K: int          # routed per token
     F: int          # expert FFN width
     act: str        # "f32" | "bf16"
-    wdt: str        # "f32" | "bf16" | "int4"
+    wdt: str        # "f32" | "bf16" | "int4" | "int3" | "int2"
     zipf: bool = False   # Zipf(1.1) per-expert router offset
 
 
@@ -52,6 +52,10 @@ PREFILL_BF16 = LayerShape(T=8192, H=2048, E=512, K=10, F=512, act="bf16", wdt="b
 STACK_INT4_LAYERS = 48
 STACK_INT4_PREFILL = LayerShape(T=8192, H=2048, E=256, K=10, F=512, act="bf16", wdt="int4")
 STACK_INT4_VERIFY = LayerShape(T=5, H=2048, E=256, K=10, F=512, act="bf16", wdt="int4")
+# the same verify step with lower-bit experts
+STACK_INT3_VERIFY = LayerShape(T=5, H=2048, E=256, K=10, F=512, act="bf16", wdt="int3")
+STACK_INT2_VERIFY = LayerShape(T=5, H=2048, E=256, K=10, F=512, act="bf16", wdt="int2")
+LOWBIT = {"int2": 2, "int3": 3}
 FREQ_L, FREQ_T, FREQ_E, FREQ_K, FREQ_KEEP = 48, 262144, 512, 10, 256
 
 
@@ -108,6 +112,54 @@ def int4_quantize(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return packed, d16
 
 
+def lowbit_levels_np(w: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric `bits`-bit quantisation in blocks of 32 along the last axis:
+    d = fp16(max|w| / (2^(bits-1) - 1)), q = clamp(rne(w / d), -2^(bits-1),
+    2^(bits-1) - 1), level u = q + 2^(bits-1).  Returns (u uint8 [..., cols],
+    scales float16 [..., cols/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    cols = w.shape[-1]
+    assert cols % INT4_BLOCK == 0
+    half = 1 << (bits - 1)
+    blk = w.reshape(*w.shape[:-1], cols // INT4_BLOCK, INT4_BLOCK)
+    amax = np.abs(blk).max(axis=-1)
+    d16 = (amax / np.float32(half - 1)).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    safe = np.where(d32 == 0, np.float32(1.0), d32)
+    q = np.rint(blk / safe[..., None]).astype(np.int32)
+    q = np.where(d32[..., None] == 0, 0, q)
+    u = (np.clip(q, -half, half - 1) + half).reshape(*w.shape[:-1], cols).astype(np.uint8)
+    return u, d16
+
+
+def lowbit_pack_np(u: np.ndarray, bits: int) -> np.ndarray:
+    """Pack levels u [..., cols] (0 <= u < 2^bits) into rows of cols*bits/8
+    bytes: the low two bits as little-endian 32-bit words of 16 elements
+    (element 4k + j of a word in byte j, bits 2k..2k+1), then for int3 the third
+    bit as words of 32 elements (element 16g + 4k + j in byte j, bit 4g + k)."""
+    u = np.asarray(u, dtype=np.uint8)
+    lead, cols = u.shape[:-1], u.shape[-1]
+    lo = (u & 3).reshape(*lead, cols // 16, 4, 4)                 # [word][k][j]
+    plane2 = np.zeros((*lead, cols // 16, 4), dtype=np.uint8)
+    for k in range(4):
+        plane2 |= lo[..., k, :] << (2 * k)
+    out = plane2.reshape(*lead, cols // 4)
+    if bits == 3:
+        hi = (u >> 2).reshape(*lead, cols // 32, 2, 4, 4)         # [word][g][k][j]
+        plane3 = np.zeros((*lead, cols // 32, 4), dtype=np.uint8)
+        for g in range(2):
+            for k in range(4):
+                plane3 |= hi[..., g, k, :] << (4 * g + k)
+        out = np.concatenate([out, plane3.reshape(*lead, cols // 8)], axis=-1)
+    return out
+
+
+def lowbit_quantize(w: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """(packed uint8 [..., cols*bits/8], scales float16 [..., cols/32])."""
+    u, d = lowbit_levels_np(w, bits)
+    return lowbit_pack_np(u, bits), d
+
+
 # ---------------------------------------------------------------- host generators
 def zipf_bias_np(E: int, seed: int, cfg: int, layer: int) -> np.ndarray:
     """Per-expert router offset b[e] = -s * ln(1 + pi(e)) (log of a Zipf(s) pmf,
@@ -148,6 +200,11 @@ def make_host_layer(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0,
         out.wg, out.sg = int4_quantize(wg)
         out.wu, out.su = int4_quantize(wu)
         out.wd, out.sd = int4_quantize(wd)
+    elif s.wdt in LOWBIT:
+        b = LOWBIT[s.wdt]
+        out.wg, out.sg = lowbit_quantize(wg, b)
+        out.wu, out.su = lowbit_quantize(wu, b)
+        out.wd, out.sd = lowbit_quantize(wd, b)
     return out
 
 
@@ -212,6 +269,35 @@ def int4_quantize_torch(w):
     return packed.contiguous(), d16.contiguous()
 
 
+def lowbit_quantize_torch(w, bits: int):
+    """Torch version of lowbit_quantize (same format); w float32 [..., cols]."""
+    torch = _torch()
+    cols = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    half = 1 << (bits - 1)
+    blk = w.reshape(*lead, cols // INT4_BLOCK, INT4_BLOCK)
+    amax = blk.abs().amax(dim=-1)
+    d16 = (amax / float(half - 1)).to(torch.float16)
+    d32 = d16.to(torch.float32)
+    safe = torch.where(d32 == 0, torch.ones_like(d32), d32)
+    q = torch.round(blk / safe.unsqueeze(-1))
+    q = torch.where(d32.unsqueeze(-1) == 0, torch.zeros_like(q), q)
+    u = (q.clamp_(-half, half - 1) + half).to(torch.uint8).reshape(*lead, cols)
+    lo = (u & 3).reshape(*lead, cols // 16, 4, 4)
+    plane2 = torch.zeros(lead + (cols // 16, 4), dtype=torch.uint8, device=w.device)
+    for k in range(4):
+        plane2 |= lo[..., k, :] << (2 * k)
+    out = plane2.reshape(*lead, cols // 4)
+    if bits == 3:
+        hi = (u >> 2).reshape(*lead, cols // 32, 2, 4, 4)
+        plane3 = torch.zeros(lead + (cols // 32, 4), dtype=torch.uint8, device=w.device)
+        for g in range(2):
+            for k in range(4):
+                plane3 |= hi[..., g, k, :] << (4 * g + k)
+        out = torch.cat([out, plane3.reshape(*lead, cols // 8)], dim=-1)
+    return out.contiguous(), d16.contiguous()
+
+
 @dataclasses.dataclass
 class DeviceLayer:
     shape: LayerShape
@@ -241,14 +327,15 @@ def make_device_weights(s: LayerShape, seed: int, cfg: int, layer: int, device, 
             dt = torch.float32 if s.wdt == "f32" else torch.bfloat16
             res[tid] = (_dev_normal(shp, sigma_w, seed, cfg, layer, tid, device, dt, chunk_rows=32), None)
         else:
+            bits = LOWBIT.get(s.wdt, 4)
             g = torch.Generator(device=device)
             g.manual_seed(torch_seed(seed, cfg, layer, tid))
-            packed = torch.empty(shp[:-1] + (shp[-1] // 2,), dtype=torch.uint8, device=device)
+            packed = torch.empty(shp[:-1] + (shp[-1] * bits // 8,), dtype=torch.uint8, device=device)
             scales = torch.empty(shp[:-1] + (shp[-1] // INT4_BLOCK,), dtype=torch.float16, device=device)
             for i in range(0, shp[0], 32):
                 j = min(shp[0], i + 32)
                 blk = torch.randn((j - i,) + shp[1:], generator=g, device=device, dtype=torch.float32).mul_(sigma_w)
-                p, d = int4_quantize_torch(blk)
+                p, d = int4_quantize_torch(blk) if bits == 4 else lowbit_quantize_torch(blk, bits)
                 packed[i:j].copy_(p)
                 scales[i:j].copy_(d)
                 del blk, p, d
@@ -289,11 +376,12 @@ def expert_bytes(s: LayerShape) -> int:
         return 4 * n
     if s.wdt == "bf16":
         return 2 * n
-    return n // 2 + 2 * (n // INT4_BLOCK)
+    return n * LOWBIT.get(s.wdt, 4) // 8 + 2 * (n // INT4_BLOCK)
 
 
 def describe() -> str:
     return ("x ~ N(0,1); router and expert weights ~ N(0,0.02); fp32 draws cast by RNE to bf16 "
-            "or quantised to int4 (blocks of 32 along the input dim, fp16 scale = max|w|/7); "
+            "or quantised to int4 / int3 / int2 (blocks of 32 along the input dim, fp16 scale = max|w|/7, "
+            "/3, /1); "
             "Zipf(1.1) router offset b[e] = -1.1 ln(1+pi(e)) with a seeded permutation pi")
 

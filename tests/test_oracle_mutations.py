@@ -25,6 +25,9 @@ MUTANTS = {
     "dropped_residual": ("acc[h] + (res ?", "acc[h] + (0 ?"),
     "bias_ignored": ("if (bias) l = l + bias[e];", ";"),
     "up_used_twice": ("u += xv * weight_value(wu, su,", "u += xv * weight_value(wg, sg,"),
+    "int2_byte_and_pair_swapped": ("int u = (row[word * 4 + j] >> (2 * k)) & 3;", "int u = (row[word * 4 + k] >> (2 * j)) & 3;"),
+    "int3_third_bit_order": ("(third[word3 * 4 + j3] >> (4 * g + k3)) & 1", "(third[word3 * 4 + j3] >> (4 * k3 + g)) & 1"),
+    "lowbit_zero_point_off_by_one": ("c) - (1 << (bits - 1));", "c) - (1 << (bits - 1)) + 1;"),
     "keep_map_by_rank": ("if (r[e] < keep) keep_map[(int64_t)l * keep + n++] = e;",
                          "if (r[e] < keep) keep_map[(int64_t)l * keep + r[e]] = e;"),
 }

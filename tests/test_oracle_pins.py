@@ -91,6 +91,56 @@ def test_int4_numpy_and_torch_quantisers_agree():
     assert np.array_equal(p, pt.numpy()) and np.array_equal(s.view(np.uint16), st.numpy().view(np.uint16))
 
 
+def test_lowbit_formats_hand_bytes(orc):
+    """int2 / int3 rows written out by hand from the layout rule (R16): the low
+    two bits in 32-bit little-endian words of 16 elements, element 4k + j in
+    byte j at bits 2k; int3's third bit in words of 32, element 16g + 4k + j in
+    byte j at bit 4g + k; value d (u - 2) or d (u - 4).  The cases separate j
+    from k and g, and the two scales of a 64-element row."""
+    one, half, two, four = 0x3C00, 0x3800, 0x4000, 0x4400
+    cases = [
+        # (bits, row bytes, fp16 scales, expected values)
+        (2, [0x00, 0x55, 0xAA, 0xFF] * 2, [one], [(i % 4) - 2 for i in range(32)]),
+        (2, [0xE4] * 8, [half], [((i % 16) // 4 - 2) * 0.5 for i in range(32)]),
+        (2, [0xFF] * 16, [one, two], [1.0] * 32 + [2.0] * 32),
+        (3, [0x00, 0x55, 0xAA, 0xFF] * 2 + [0xF0] * 4, [one], [(i % 4) + (4 if i >= 16 else 0) - 4 for i in range(32)]),
+        (3, [0x00] * 8 + [0x22] * 4, [one], [0 if (i % 16) // 4 == 1 else -4 for i in range(32)]),
+        (3, [0x00] * 8 + [0x00, 0x00, 0xFF, 0x00], [four], [0 if i % 4 == 2 else -16 for i in range(32)]),
+    ]
+    for bits, row, sc, want in cases:
+        packed = np.array([row], np.uint8)
+        scales = np.array([sc], np.uint16)
+        got = orc.lowbit_dequant(packed, scales, bits)[0]
+        assert got.tolist() == [float(v) for v in want], (bits, row)
+        # the input generator's packer writes the same bytes for these levels
+        d = np.array([orc.fp16_value(v) for v in sc])
+        u = np.rint(np.array(want, np.float64) / np.repeat(d, 32)).astype(np.int64) + (1 << (bits - 1))
+        assert synth.lowbit_pack_np(u[None, :].astype(np.uint8), bits)[0].tolist() == row
+
+
+def test_lowbit_round_trip_and_torch_agree(orc):
+    rng = np.random.default_rng(11)
+    for bits in (2, 3):
+        half = 1 << (bits - 1)
+        qq = rng.integers(-(half - 1), half, size=(5, 64))   # levels the scale max|w| / (half - 1) reaches exactly
+        qq[:, 0], qq[:, 32] = half - 1, -(half - 1)
+        dd = np.array([2.0 ** -7, 3 * 2.0 ** -10, 5 * 2.0 ** -12, 2.0 ** -5, 2.0 ** -9], np.float32)
+        w = qq.astype(np.float32) * dd[:, None]
+        p, sc = synth.lowbit_quantize(w, bits)
+        assert p.shape == (5, 64 * bits // 8) and sc.shape == (5, 2)
+        assert np.array_equal(orc.lowbit_dequant(p, sc, bits), w.astype(np.float64))
+        z = synth.lowbit_quantize(np.zeros((1, 32), np.float32), bits)
+        assert z[1][0, 0] == 0 and np.all(orc.lowbit_dequant(*z, bits) == 0)
+        r = (rng.standard_normal((4, 96)) * 0.02).astype(np.float32)
+        pn, sn = synth.lowbit_quantize(r, bits)
+        pt, st = synth.lowbit_quantize_torch(torch.from_numpy(r), bits)
+        assert np.array_equal(pn, pt.numpy()) and np.array_equal(sn.view(np.uint16), st.numpy().view(np.uint16))
+        # every value within half a step of its block's scale
+        deq = orc.lowbit_dequant(pn, sn, bits)
+        step = np.repeat(sn.astype(np.float64), 32, axis=1)
+        assert np.all(np.abs(deq - r) <= 0.5 * step * (1 + 1e-3))
+
+
 # ------------------------------------------------------------------ a1: router logits
 def _nearest_f32(fr: Fraction) -> np.float32:
     """Correctly rounded fp32 of an exact rational (ties to even), by exact comparison."""
@@ -360,6 +410,21 @@ def test_int4_path_equals_fp32_path_on_dequantised_weights(orc):
     for p, sc in ((L.wg, L.sg), (L.wd, L.sd)):
         assert np.array_equal(deq(p, sc)[0], orc.int4_dequant(p[0], sc[0]))
     a = orc.layer_rows(L.x, idx, w, W4)
+    b = orc.layer_rows(L.x, idx, w, Wf)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("wdt", ["int3", "int2"])
+def test_lowbit_path_equals_fp32_path_on_dequantised_weights(orc, wdt):
+    s = synth.LayerShape(T=6, H=64, E=4, K=2, F=64, act="bf16", wdt=wdt)
+    L = synth.make_host_layer(s, seed=2, cfg=9)
+    idx, w, _ = orc.route(L.x, L.wr, 2)
+    Wq = orc.Weights(wdt, L.wg, L.wu, L.wd, L.sg, L.su, L.sd)
+    bits = synth.LOWBIT[wdt]
+    Wf = orc.Weights("f32", *(orc.lowbit_dequant(p.reshape(-1, p.shape[-1]), sc.reshape(-1, sc.shape[-1]), bits)
+                              .reshape(p.shape[:-1] + (p.shape[-1] * 8 // bits,)).astype(np.float32)
+                              for p, sc in ((L.wg, L.sg), (L.wu, L.su), (L.wd, L.sd))))
+    a = orc.layer_rows(L.x, idx, w, Wq)
     b = orc.layer_rows(L.x, idx, w, Wf)
     assert np.array_equal(a, b)
 
