@@ -129,7 +129,7 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
     for L in layers[1:]:
         L.x = x
     torch.cuda.synchronize()
-    wdt = {"bf16": moe.BF16, "int4": moe.INT4_B32}[shape.wdt]
+    wdt = {"bf16": moe.BF16, "int4": moe.INT4_B32, "int3": moe.INT3_B32, "int2": moe.INT2_B32}[shape.wdt]
     lw = moe.LayerWorkspace(shape.T, shape.H, shape.E, shape.K, shape.F, x_dtype=x.dtype, w_dtype=wdt)
 
     def step(L):
@@ -319,7 +319,8 @@ def bench_stack(torch, moe, synth, shape, steps, warmup, use_graph, name, steere
     vs = [torch.from_numpy(synth.steer_vector(shape.H, layer=l)).cuda() if l < steered else None for l in range(Ls)]
     x0 = layers[0].x
     torch.cuda.synchronize()
-    lw = moe.LayerWorkspace(shape.T, shape.H, shape.E, shape.K, shape.F, x_dtype=torch.bfloat16, w_dtype=moe.INT4_B32)
+    wdt = {"int4": moe.INT4_B32, "int3": moe.INT3_B32, "int2": moe.INT2_B32}[shape.wdt]
+    lw = moe.LayerWorkspace(shape.T, shape.H, shape.E, shape.K, shape.F, x_dtype=torch.bfloat16, w_dtype=wdt)
     h = torch.empty_like(x0)
 
     def run(steer):
@@ -336,10 +337,11 @@ def bench_stack(torch, moe, synth, shape, steps, warmup, use_graph, name, steere
         return dt / n * 1e3, n, wall
 
     ms, n, wall = run(False)
-    ms_s, _, _ = run(True)
     res = dict(name=name, T=shape.T, layers=Ls, ms_per_step=ms, ms_per_layer=ms / Ls,
-               value=shape.T * Ls / (ms / 1e3), unit="tokens/s per MoE layer (48-layer stack)", steps=n, wall_s=wall,
-               steered_layers=steered, ms_per_step_steered=ms_s, steer_cost_frac=ms_s / ms - 1.0)
+               value=shape.T * Ls / (ms / 1e3), unit="tokens/s per MoE layer (48-layer stack)", steps=n, wall_s=wall)
+    if steered:
+        ms_s, _, _ = run(True)
+        res.update(steered_layers=steered, ms_per_step_steered=ms_s, steer_cost_frac=ms_s / ms - 1.0)
     del layers
     return res
 
@@ -374,7 +376,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workloads", default="verify,prefill,freq,stack")
+    ap.add_argument("--workloads", default="verify,prefill,freq,stack,lowbit")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of HIP graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -423,6 +425,24 @@ def main():
             log(f"[stack T={shp.T}] {r['ms_per_step']:.3f} ms/step, {r['ms_per_step_steered']:.3f} ms steered")
             also.append(r)
             torch.cuda.empty_cache()
+    if "lowbit" in wl:
+        # the verify step of the pruned layer with int4, int3 and int2 experts: one
+        # layer over 8 rotating weight sets, and the 48-layer stack
+        for shp in (synth.STACK_INT4_VERIFY, synth.STACK_INT3_VERIFY, synth.STACK_INT2_VERIFY):
+            r = bench_layer(torch, moe, synth, shp, 5, args.steps, args.warmup, N_SETS, use_graph,
+                            f"verify step 5 tok, E256 top-10, {shp.wdt} experts")
+            r["unit"] = "tokens/s"
+            r["ffn_hbm_frac"] = r["ffn_hbm_gbs"] / HBM_PEAK_GBS
+            log(f"[{shp.wdt} verify] {r['ms_per_step']*1e3:.1f} us/step  ffn {r['parts_us']['ffn']:.1f} us "
+                f"{r['ffn_hbm_gbs']:.0f} GB/s")
+            also.append(r)
+            torch.cuda.empty_cache()
+            if shp.wdt != "int4":
+                r = bench_stack(torch, moe, synth, shp, max(3, args.steps // 40), 1, use_graph,
+                                f"pruned 48-layer {shp.wdt} stack, 5-tok verify", steered=0)
+                log(f"[{shp.wdt} stack T={shp.T}] {r['ms_per_step']:.3f} ms/step")
+                also.append(r)
+                torch.cuda.empty_cache()
 
     if main_res is None:          # a partial run (e.g. under a profiler): report the first workload
         main_res = also.pop(0) if also else None

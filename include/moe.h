@@ -64,7 +64,17 @@ typedef enum {
      * (reduction) dimension of each out x in weight row: the element is
      * d * (nibble - 8), d the block's IEEE fp16 scale; byte j of a row holds
      * element 2j in its low nibble and 2j+1 in its high nibble. */
-    MOE_INT4_B32 = 2
+    MOE_INT4_B32 = 2,
+    /* Lower-bit variants of the same block scheme (32 consecutive elements
+     * along the input dimension share an fp16 scale d): the element is
+     * d * (u - 2) (int2) or d * (u - 4) (int3), u its stored level.  A row
+     * of n elements is n/4 bytes of the low two bits of every level, as
+     * 32-bit little-endian words of 16 elements (element 4k + j of a word in
+     * byte j, bits 2k and 2k+1); an int3 row continues with n/8 bytes of the
+     * third bits, as words of 32 elements (element 16g + 4k + j of a word in
+     * byte j, bit 4g + k). */
+    MOE_INT2_B32 = 3,
+    MOE_INT3_B32 = 4
 } moe_dtype;
 
 typedef void* moe_stream; /* hipStream_t */
@@ -72,7 +82,8 @@ typedef void* moe_stream; /* hipStream_t */
 /* One layer's expert weights, E experts of width F over hidden size H.
  *   F32 / BF16:  w_gate, w_up [E][F][H];  w_down [E][H][F];  s_* must be NULL.
  *   INT4_B32:    w_gate, w_up [E][F][H/2] bytes, s_gate, s_up [E][F][H/32] fp16;
- *                w_down [E][H][F/2] bytes, s_down [E][H][F/32] fp16. */
+ *                w_down [E][H][F/2] bytes, s_down [E][H][F/32] fp16.
+ *   INT3_B32 / INT2_B32: as INT4_B32 with rows of 3n/8 / n/4 bytes. */
 typedef struct {
     int32_t dtype; /* moe_dtype */
     const void* w_gate;
@@ -139,7 +150,10 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
  *   x        [T][H] activations, MOE_F32 or MOE_BF16.
  *   y_perm   [T*K][H] out, y_dtype MOE_F32 or MOE_BF16.
  * Built combinations: (x F32, weights F32, y F32), (x BF16, weights BF16,
- * y BF16 or F32), (x BF16, weights INT4_B32, y BF16 or F32).
+ * y BF16 or F32), (x BF16, weights INT4_B32, y BF16 or F32), and for the
+ * verify and decode steps (x BF16, weights INT3_B32 or INT2_B32, y BF16 or
+ * F32) with T <= 8, H = 2048, F = 512 (the lower-bit expert variant; other
+ * shapes return MOE_ERR_UNSUPPORTED).
  * Unsupported: H or F not a multiple of 64. */
 size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_t F, int32_t x_dtype,
                               int32_t w_dtype);

@@ -135,10 +135,15 @@ moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, 
         return MOE_ERR_INVALID_ARG;
     if (!w || !offsets || (T > 0 && (!x || !perm || !y_perm))) return MOE_ERR_INVALID_ARG;
     if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+    const bool quant = w->dtype == MOE_INT4_B32 || w->dtype == MOE_INT3_B32 || w->dtype == MOE_INT2_B32;
     if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (y_dtype != MOE_F32 && y_dtype != MOE_BF16) ||
-        (w->dtype != MOE_F32 && w->dtype != MOE_BF16 && w->dtype != MOE_INT4_B32))
+        (w->dtype != MOE_F32 && w->dtype != MOE_BF16 && !quant))
         return MOE_ERR_INVALID_ARG;
-    if (w->dtype == MOE_INT4_B32 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    if (quant && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    // int3 / int2: the few-token (verify, decode) streaming kernels
+    if ((w->dtype == MOE_INT3_B32 || w->dtype == MOE_INT2_B32) &&
+        (x_dtype != MOE_BF16 || !ffn_stream_q4_eligible(T, K, E, H, F)))
+        return MOE_ERR_UNSUPPORTED;
     if ((int64_t)T * K * H > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
     // built combinations
     if (x_dtype == MOE_F32) {

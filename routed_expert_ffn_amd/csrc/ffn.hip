@@ -20,7 +20,7 @@
 #include "common.h"
 #include "launch.h"
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_INT4 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_INT4 = 2, DT_INT2 = 3, DT_INT3 = 4 };
 
 constexpr int G_BM = 64, G_BNF = 64, G_BK = 64, G_LD = G_BK + 8;   // gate/up tile
 constexpr int D_BM = 64, D_BN = 128, D_BK = 64, D_LD = D_BK + 8;   // down tile
@@ -367,6 +367,10 @@ hipError_t launch_ffn(const void* x, int x_dtype, int w_dtype, const void* wg, c
                            offsets, n, H, F, E, (float*)y);
         return hipGetLastError();
     }
+    // int3 / int2 experts: the verify-step streaming kernels only (checked by the caller)
+    if (w_dtype == DT_INT2 || w_dtype == DT_INT3)
+        return launch_ffn_stream_q4(x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y, y_dtype == DT_BF16, ws,
+                                    st, w_dtype == DT_INT2 ? 2 : 3);
     if (ffn_small_eligible(T, H, F))
         return launch_ffn_small(x, w_dtype, wg, wu, wd, sg, su, sd, offsets, perm, T, K, H, F, E, y,
                                 y_dtype == DT_BF16, ws, st);

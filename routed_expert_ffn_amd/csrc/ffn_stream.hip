@@ -1,5 +1,6 @@
 // ffn_stream.hip -- the expert FFN for a handful of tokens (T <= 8: the
-// speculative verify step of 4 drafts + 1, and decode), bf16 weights.
+// speculative verify step of 4 drafts + 1, and decode); bf16 weights, and
+// int4 / int3 / int2 blocks of 32 with an fp16 scale.
 //
 // Per touched expert e with rows p in [off_e, off_e + n_e) (token perm[p] / K):
 //   a[p] = bf16(silu(x Wg_e^T) * (x Wu_e^T)),   y_perm[p] = a[p] Wd_e^T
@@ -316,6 +317,56 @@ MOE_DEV float dot_block_q4(uint4 q, const uint16_t* __restrict__ xl) {
     return d;
 }
 MOE_DEV uint16_t ldnt_u16(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+MOE_DEV uint32_t ldnt_u32(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
+typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
+MOE_DEV u32x2_v ldnt8(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x2_v*>(p)); }
+
+// Lower-bit blocks (int2: value d (u - 2); int3: d (u - 4)).  A block's 32
+// levels: two 32-bit words of the low two bits (16 elements each, element
+// 4k + j of a word in byte j, bits 2k..2k+1) and, for int3, one word of third
+// bits (element 16g + 4k + j in byte j, bit 4g + k).  Shifting a low word by
+// 2k and masking 0x03030303 leaves elements 4k..4k+3 one per byte (the third
+// bits join them the same way), and a byte permute spreads two of them into
+// the bf16 pair 128 + u, so the dot product takes the activations in their
+// natural order:  sum_k x w = d (D - (128 + 2^(bits-1)) S).
+template <int QB>
+MOE_DEV float dot_block_low(const uint32_t (&q)[QB], const uint16_t* __restrict__ xl) {
+    float d = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; g++) {
+        const uint4 xa = *reinterpret_cast<const uint4*>(xl + g * 16);
+        const uint4 xb = *reinterpret_cast<const uint4*>(xl + g * 16 + 8);
+        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            uint32_t m = (q[g] >> (2 * k)) & 0x03030303u;
+            if constexpr (QB == 3) m |= ((q[2] >> (4 * g + k)) & 0x01010101u) << 2;
+            d = dot2bf(__builtin_amdgcn_perm(m, m, 0x0C010C00u) | 0x43004300u, xw[2 * k], d);
+            d = dot2bf(__builtin_amdgcn_perm(m, m, 0x0C030C02u) | 0x43004300u, xw[2 * k + 1], d);
+        }
+    }
+    return d;
+}
+// one lane's block: 4 dwords (int4), 2 (int2) or 3 (int3)
+template <int QB> struct QWords { static constexpr int n = QB == 4 ? 4 : QB; };
+template <int QB>
+MOE_DEV float dot_block(const uint32_t (&q)[QWords<QB>::n], const uint16_t* __restrict__ xl) {
+    if constexpr (QB == 4) return dot_block_q4(make_uint4(q[0], q[1], q[2], q[3]), xl);
+    else return dot_block_low<QB>(q, xl);
+}
+// the lane's block of a row of n inputs at `row` (bytes n*QB/8), block b
+template <int QB>
+MOE_DEV void load_block(uint32_t (&q)[QWords<QB>::n], const uint8_t* __restrict__ row, int n, int b) {
+    if constexpr (QB == 4) {
+        const uint4 v = ldnt16(row + b * 16);
+        q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+    } else {
+        const u32x2_v v = ldnt8(row + b * 8);
+        q[0] = v.x; q[1] = v.y;
+        if constexpr (QB == 3) q[2] = ldnt_u32(row + n / 4 + b * 4);
+    }
+}
+template <int QB> constexpr float zero_level() { return 128.0f + (float)(1 << (QB - 1)); }
 
 // sums of every 32-element block of `rows` LDS rows of `cols` bf16 into sums[row][cols/32]
 MOE_DEV void block_sums(const uint16_t* __restrict__ rowsp, int rows, int cols, float* __restrict__ sums) {
@@ -339,10 +390,10 @@ MOE_DEV float group16_tr_reduce(float (&v)[V]) {
 }
 }  // namespace
 
-// gate/up, int4.  Item = FR gate rows and the same FR up rows over all of
-// H = CH x 2048 (a lane: one quant block per row and chunk).
-template <int NT, int CH, int FR, int RING>
-__global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg,
+// gate/up, int4 / int3 / int2 (QB bits).  Item = FR gate rows and the same FR
+// up rows over all of H = CH x 2048 (a lane: one quant block per row and chunk).
+template <int NT, int CH, int FR, int RING, int QB>
+__global__ __launch_bounds__(256, (QB == 4 ? 1 : 2)) void k_gateup_stream_q4(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg,
                                                           const uint8_t* __restrict__ wu, const uint16_t* __restrict__ sg,
                                                           const uint16_t* __restrict__ su,
                                                           const int32_t* __restrict__ offsets,
@@ -369,7 +420,8 @@ __global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __rest
     const int it = blockIdx.x * 4 + wave;
     if (it >= n_items) return;
 
-    struct Buf { uint4 q[2 * FR][CH]; uint16_t d[2 * FR][CH]; };
+    constexpr int QW = QWords<QB>::n;
+    struct Buf { uint32_t q[2 * FR][CH][QW]; uint16_t d[2 * FR][CH]; };
     Buf wbuf[RING];
     auto load = [&](int item, Buf& b) __attribute__((always_inline)) {
         const long row0 = (long)list[item / tpe].x * F + (item % tpe) * FR;
@@ -377,8 +429,8 @@ __global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __rest
         for (int r = 0; r < FR; r++)
 #pragma unroll
             for (int c = 0; c < CH; c++) {
-                b.q[r][c] = ldnt16(wg + (row0 + r) * (H / 2) + c * 1024 + l * 16);
-                b.q[FR + r][c] = ldnt16(wu + (row0 + r) * (H / 2) + c * 1024 + l * 16);
+                load_block<QB>(b.q[r][c], wg + (row0 + r) * (H * QB / 8), H, c * 64 + l);
+                load_block<QB>(b.q[FR + r][c], wu + (row0 + r) * (H * QB / 8), H, c * 64 + l);
                 b.d[r][c] = ldnt_u16(sg + (row0 + r) * (H / 32) + c * 64 + l);
                 b.d[FR + r][c] = ldnt_u16(su + (row0 + r) * (H / 32) + c * 64 + l);
             }
@@ -400,8 +452,8 @@ __global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __rest
                     const float S = xsum[tok * (H / 32) + c * 64 + l];
 #pragma unroll
                     for (int r = 0; r < 2 * FR; r++) {
-                        const float D = dot_block_q4(b.q[r][c], xl);
-                        acc[r * NT + t] = fmaf(fp16_to_f32(b.d[r][c]), fmaf(-136.0f, S, D), acc[r * NT + t]);
+                        const float D = dot_block<QB>(b.q[r][c], xl);
+                        acc[r * NT + t] = fmaf(fp16_to_f32(b.d[r][c]), fmaf(-zero_level<QB>(), S, D), acc[r * NT + t]);
                     }
                 }
             }
@@ -416,9 +468,10 @@ __global__ __launch_bounds__(256) void k_gateup_stream_q4(const uint16_t* __rest
     ring_walk<RING>(it, W, n_items, wbuf, load, compute);
 }
 
-// down, int4, F = 512: a 1 KB instruction covers 4 rows of Wd (16 lanes x one
-// quant block each).  Item = I instructions = 4I hidden rows.
-template <int NT, int I, int YBF16, int RING>
+// down, int4 / int3 / int2 (QB bits), F = 512: a wave instruction covers 4
+// rows of Wd (16 lanes x one quant block each).  Item = I instructions = 4I
+// hidden rows.
+template <int NT, int I, int YBF16, int RING, int QB>
 __global__ __launch_bounds__(256) void k_down_stream_q4(const uint16_t* __restrict__ abuf, const uint8_t* __restrict__ wd,
                                                         const uint16_t* __restrict__ sd,
                                                         const int32_t* __restrict__ offsets, int nrows, int E, int H,
@@ -443,13 +496,14 @@ __global__ __launch_bounds__(256) void k_down_stream_q4(const uint16_t* __restri
     if (it >= n_items) return;
     const int g = l >> 4, b = l & 15;            // row within an instruction, quant block within the row
 
-    struct Buf { uint4 q[I]; uint16_t d[I]; };
+    constexpr int QW = QWords<QB>::n;
+    struct Buf { uint32_t q[I][QW]; uint16_t d[I]; };
     Buf wbuf[RING];
     auto load = [&](int item, Buf& bf) __attribute__((always_inline)) {
         const long row0 = (long)list[item / tpe].x * H + (item % tpe) * (4 * I) + g;
 #pragma unroll
         for (int i = 0; i < I; i++) {
-            bf.q[i] = ldnt16(wd + (row0 + 4 * i) * (F / 2) + b * 16);
+            load_block<QB>(bf.q[i], wd + (row0 + 4 * i) * (F * QB / 8), F, b);
             bf.d[i] = ldnt_u16(sd + (row0 + 4 * i) * NB + b);
         }
     };
@@ -468,8 +522,8 @@ __global__ __launch_bounds__(256) void k_down_stream_q4(const uint16_t* __restri
                 const float S = asum[(off + t) * NB + b];
 #pragma unroll
                 for (int i = 0; i < I; i++) {
-                    const float D = dot_block_q4(bf.q[i], al);
-                    acc[i * NT + t] = fmaf(fp16_to_f32(bf.d[i]), fmaf(-136.0f, S, D), acc[i * NT + t]);
+                    const float D = dot_block<QB>(bf.q[i], al);
+                    acc[i * NT + t] = fmaf(fp16_to_f32(bf.d[i]), fmaf(-zero_level<QB>(), S, D), acc[i * NT + t]);
                 }
             }
         }
@@ -552,15 +606,17 @@ hipError_t stream_nt(int grid, hipStream_t st, const uint16_t* x, const void* wg
 }  // namespace
 
 namespace {
-constexpr int Q4_FR = 4, Q4_I = 2, Q4_RING = 2;
+constexpr int Q4_FR = 4, Q4_I = 2;
+// weight items in flight per wave: int4 items are the largest
+constexpr int Q_RING = 2;   // weight items per wave: one in flight while one multiplies
 size_t gu_lds_q4(int T, int K, int H) { return (size_t)T * H * 2 + (size_t)T * (H / 32) * 4 + (size_t)T * K * 20; }
 size_t dn_lds_q4(int T, int K) { return (size_t)T * K * 512 * 2 + (size_t)T * K * 16 * 4 + (size_t)T * K * 16; }
 
-template <int NT, int CH>
+template <int NT, int CH, int QB>
 hipError_t gu_launch_q4(int grid, hipStream_t st, const uint16_t* x, const void* wg, const void* wu, const void* sg,
                         const void* su, const int32_t* offsets, const int32_t* perm, int T, int K, int E, int F,
                         uint16_t* abuf) {
-    auto kern = k_gateup_stream_q4<NT, CH, Q4_FR, Q4_RING>;
+    auto kern = k_gateup_stream_q4<NT, CH, Q4_FR, Q_RING, QB>;
     const size_t lds = gu_lds_q4(T, K, CH * 2048);
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -568,10 +624,10 @@ hipError_t gu_launch_q4(int grid, hipStream_t st, const uint16_t* x, const void*
                        (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, T, K, E, F, abuf);
     return hipSuccess;
 }
-template <int NT, int YB>
+template <int NT, int YB, int QB>
 hipError_t dn_launch_q4(int grid, hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd,
                         const int32_t* offsets, int T, int K, int E, int H, void* y) {
-    auto kern = k_down_stream_q4<NT, Q4_I, YB, Q4_RING>;
+    auto kern = k_down_stream_q4<NT, Q4_I, YB, Q_RING, QB>;
     const size_t lds = dn_lds_q4(T, K);
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -579,14 +635,23 @@ hipError_t dn_launch_q4(int grid, hipStream_t st, const uint16_t* abuf, const vo
                        T * K, E, H, y);
     return hipSuccess;
 }
-template <int NT>
+template <int NT, int QB>
 hipError_t stream_q4_nt(int grid, hipStream_t st, const uint16_t* x, const void* wg, const void* wu, const void* wd,
                         const void* sg, const void* su, const void* sd, const int32_t* offsets, const int32_t* perm,
                         int T, int K, int E, int H, int F, void* y, int y_bf16, uint16_t* abuf) {
-    hipError_t e = gu_launch_q4<NT, 1>(grid, st, x, wg, wu, sg, su, offsets, perm, T, K, E, F, abuf);   // H = 2048
+    hipError_t e = gu_launch_q4<NT, 1, QB>(grid, st, x, wg, wu, sg, su, offsets, perm, T, K, E, F, abuf);   // H = 2048
     if (e != hipSuccess) return e;
-    return y_bf16 ? dn_launch_q4<NT, 1>(grid, st, abuf, wd, sd, offsets, T, K, E, H, y)
-                  : dn_launch_q4<NT, 0>(grid, st, abuf, wd, sd, offsets, T, K, E, H, y);
+    return y_bf16 ? dn_launch_q4<NT, 1, QB>(grid, st, abuf, wd, sd, offsets, T, K, E, H, y)
+                  : dn_launch_q4<NT, 0, QB>(grid, st, abuf, wd, sd, offsets, T, K, E, H, y);
+}
+template <int QB>
+hipError_t stream_q_bits(int grid, hipStream_t st, const void* x, const void* wg, const void* wu, const void* wd,
+                         const void* sg, const void* su, const void* sd, const int32_t* offsets, const int32_t* perm,
+                         int T, int K, int E, int H, int F, void* y, int y_bf16, uint16_t* abuf) {
+    return T <= 4 ? stream_q4_nt<4, QB>(grid, st, (const uint16_t*)x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H,
+                                        F, y, y_bf16, abuf)
+                  : stream_q4_nt<8, QB>(grid, st, (const uint16_t*)x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H,
+                                        F, y, y_bf16, abuf);
 }
 }  // namespace
 
@@ -597,15 +662,15 @@ bool ffn_stream_q4_eligible(int T, int K, int E, int H, int F) {
 
 hipError_t launch_ffn_stream_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
                                 const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
-                                int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st) {
+                                int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st, int bits) {
     hipError_t err;
     const int grid = stream_grid(err);
     if (err != hipSuccess) return err;
     uint16_t* abuf = (uint16_t*)ws;
-    err = T <= 4 ? stream_q4_nt<4>(grid, st, (const uint16_t*)x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y,
-                                   y_bf16, abuf)
-                 : stream_q4_nt<8>(grid, st, (const uint16_t*)x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y,
-                                   y_bf16, abuf);
+    if (bits == 4) err = stream_q_bits<4>(grid, st, x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y, y_bf16, abuf);
+    else if (bits == 3) err = stream_q_bits<3>(grid, st, x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y, y_bf16, abuf);
+    else if (bits == 2) err = stream_q_bits<2>(grid, st, x, wg, wu, wd, sg, su, sd, offsets, perm, T, K, E, H, F, y, y_bf16, abuf);
+    else return hipErrorInvalidValue;
     if (err != hipSuccess) return err;
     return hipGetLastError();
 }

@@ -44,7 +44,8 @@ size_t ffn_stream_workspace_bytes(int T, int K, int F);
 bool ffn_stream_q4_eligible(int T, int K, int E, int H, int F);
 hipError_t launch_ffn_stream_q4(const void* x, const void* wg, const void* wu, const void* wd, const void* sg,
                                 const void* su, const void* sd, const int32_t* offsets, const int32_t* perm, int T,
-                                int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st);
+                                int K, int H, int F, int E, void* y, int y_bf16, void* ws, hipStream_t st,
+                                int bits = 4);   // int4, int3 or int2 blocks
 hipError_t launch_ffn_stream(const void* x, const void* wg, const void* wu, const void* wd, const int32_t* offsets,
                              const int32_t* perm, int T, int K, int H, int F, int E, void* y, int y_bf16, void* ws,
                              hipStream_t st);

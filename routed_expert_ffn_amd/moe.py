@@ -14,7 +14,8 @@ import torch
 from . import build as _build
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-F32, BF16, INT4_B32 = 0, 1, 2
+F32, BF16, INT4_B32, INT2_B32, INT3_B32 = 0, 1, 2, 3, 4
+_QUANT_BY_BITS = {4: INT4_B32, 3: INT3_B32, 2: INT2_B32}
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_ffn_workspace_size", "moe_ffn",
@@ -201,7 +202,13 @@ def permute(topk_idx, E: int, workspace=None, stream=None, out=None):
 # ------------------------------------------------------------------ moe_ffn
 def weights_struct(wg, wu, wd, sg=None, su=None, sd=None) -> ExpertWeights:
     if wg.dtype == torch.uint8:
-        dt = INT4_B32
+        # block-quantised: the bits per weight follow from the row lengths
+        # (gate/up rows hold H inputs, H = the down matrix's row count)
+        H, F = wd.shape[1], wg.shape[1]
+        bits = wg.shape[2] * 8 // H
+        if bits not in _QUANT_BY_BITS or wg.shape[2] * 8 != bits * H or wd.shape[2] * 8 != bits * F:
+            raise ValueError(f"packed weights of shapes {tuple(wg.shape)} / {tuple(wd.shape)} are not int4, int3 or int2")
+        dt = _QUANT_BY_BITS[bits]
         for n, s in (("s_gate", sg), ("s_up", su), ("s_down", sd)):
             _need(s, n, torch.float16)
     elif wg.dtype == torch.bfloat16:
@@ -209,7 +216,7 @@ def weights_struct(wg, wu, wd, sg=None, su=None, sd=None) -> ExpertWeights:
     elif wg.dtype == torch.float32:
         dt = F32
     else:
-        raise TypeError(f"expert weights must be float32, bfloat16 or uint8 (int4), not {wg.dtype}")
+        raise TypeError(f"expert weights must be float32, bfloat16 or uint8 (int4/int3/int2), not {wg.dtype}")
     for n, t in (("w_gate", wg), ("w_up", wu), ("w_down", wd)):
         _need(t, n, wg.dtype)
     return ExpertWeights(dt, wg.data_ptr(), wu.data_ptr(), wd.data_ptr(),

@@ -97,6 +97,16 @@ def test_permute_ffn_combine_freq_reject_bad_arguments(L):
     w4 = moe.ExpertWeights(moe.INT4_B32, 0x10000, 0x10000, 0x10000, None, None, None)
     assert ffn(FAKE, moe.BF16, ctypes.byref(w4), FAKE, FAKE, 5, 10, 2048, 512, 512, FAKE, moe.BF16, FAKE, nb, None) == \
         moe.MOE_ERR_INVALID_ARG                                  # int4 needs its scales
+    for dt in (moe.INT3_B32, moe.INT2_B32):
+        wq = moe.ExpertWeights(dt, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+        nq = moe.ffn_workspace_size(9, 10, 256, 2048, 512, moe.BF16, dt)
+        assert ffn(FAKE, moe.BF16, ctypes.byref(wq), FAKE, FAKE, 9, 10, 2048, 512, 256, FAKE, moe.BF16, FAKE, nq,
+                   None) == moe.MOE_ERR_UNSUPPORTED              # int3 / int2: verify and decode steps only (T <= 8)
+        assert ffn(FAKE, moe.BF16, ctypes.byref(wq), FAKE, FAKE, 5, 10, 1024, 512, 256, FAKE, moe.BF16, FAKE, nq,
+                   None) == moe.MOE_ERR_UNSUPPORTED              # ... at H 2048, F 512
+        wn = moe.ExpertWeights(dt, 0x10000, 0x10000, 0x10000, None, None, None)
+        assert ffn(FAKE, moe.BF16, ctypes.byref(wn), FAKE, FAKE, 5, 10, 2048, 512, 256, FAKE, moe.BF16, FAKE, nq,
+                   None) == moe.MOE_ERR_INVALID_ARG              # scales required
     assert L.moe_combine(FAKE, moe.BF16, FAKE, FAKE, None, 5, 10, 2044, FAKE, moe.BF16, None) == \
         moe.MOE_ERR_UNSUPPORTED                                  # H % 8
     assert L.moe_combine(None, moe.BF16, FAKE, FAKE, None, 5, 10, 2048, FAKE, moe.BF16, None) == \

@@ -33,7 +33,8 @@ def gpu():
 def run_layer(d, residual=None, y_dtype=None):
     s = d.shape
     lw = moe.LayerWorkspace(s.T, s.H, s.E, s.K, s.F, x_dtype=d.x.dtype,
-                            w_dtype={"f32": moe.F32, "bf16": moe.BF16, "int4": moe.INT4_B32}[s.wdt],
+                            w_dtype={"f32": moe.F32, "bf16": moe.BF16, "int4": moe.INT4_B32, "int3": moe.INT3_B32,
+                                     "int2": moe.INT2_B32}[s.wdt],
                             y_dtype=y_dtype)
     out, r = moe.layer(d.x, d.wr, d.wg, d.wu, d.wd, s.K, bias=d.bias, sg=d.sg, su=d.su, sd=d.sd,
                        residual=residual, lw=lw)
@@ -88,6 +89,11 @@ SMALL = [
     # int4, T <= 8, H 2048, F 512: the streaming int4 path (one quant block per lane)
     synth.LayerShape(T=3, H=2048, E=24, K=8, F=512, act="bf16", wdt="int4"),
     synth.LayerShape(T=8, H=2048, E=6, K=4, F=512, act="bf16", wdt="int4", zipf=True),
+    # int3 / int2 (the lower-bit verify variant), T <= 8, H 2048, F 512
+    synth.LayerShape(T=3, H=2048, E=24, K=8, F=512, act="bf16", wdt="int3"),
+    synth.LayerShape(T=8, H=2048, E=6, K=4, F=512, act="bf16", wdt="int3", zipf=True),
+    synth.LayerShape(T=1, H=2048, E=40, K=10, F=512, act="bf16", wdt="int2"),
+    synth.LayerShape(T=8, H=2048, E=6, K=4, F=512, act="bf16", wdt="int2", zipf=True),
     # bf16, T <= 8, whole 1 KB rows: the streaming bf16 path
     synth.LayerShape(T=7, H=1024, E=40, K=6, F=512, act="bf16", wdt="bf16", zipf=True),
     synth.LayerShape(T=3, H=512, E=16, K=4, F=1024, act="bf16", wdt="bf16"),
@@ -348,6 +354,21 @@ def test_int4_verify_layer_full_size():
     ref_idx, ref_w, _ = oracle.route(x, wr, s.K)
     out, r = run_layer(d)
     check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    ref_out = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d))
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
+@pytest.mark.parametrize("shape", [synth.STACK_INT3_VERIFY, synth.STACK_INT2_VERIFY], ids=["int3", "int2"])
+def test_lowbit_verify_layer_full_size(shape):
+    """A layer of the pruned stack at the verify shape with int3 / int2 experts:
+    exact routing, output within the bf16 bound of the oracle on the same
+    quantised weights."""
+    d = synth.make_device_layer(shape, seed=0, cfg=5, layer=2, device="cuda")
+    torch.cuda.synchronize()
+    x, wr = to_host(d.x), to_host(d.wr)
+    ref_idx, ref_w, _ = oracle.route(x, wr, shape.K)
+    out, r = run_layer(d)
+    check_routing_and_grouping(r, ref_idx, ref_w, shape.E)
     ref_out = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d))
     assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
 
