@@ -381,8 +381,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the MoE layer is not sharded across GPUs in this build "
-              "(token rows shard with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the MoE layer is not sharded across GPUs here "
+              "(its token rows would shard with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

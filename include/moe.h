@@ -27,7 +27,7 @@
  *     error the outputs are untouched and nothing is launched.
  *       MOE_ERR_INVALID_ARG  null required pointer, non-positive size, K > E,
  *                            counts that overflow int32, unknown dtype;
- *       MOE_ERR_UNSUPPORTED  a valid request this build does not implement
+ *       MOE_ERR_UNSUPPORTED  a valid request the library does not implement
  *                            (listed per call), or a pointer not aligned to 16 B;
  *       MOE_ERR_WORKSPACE    workspace smaller than the matching *_workspace_size;
  *       MOE_ERR_HIP          a kernel launch reported an error.

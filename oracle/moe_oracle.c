@@ -22,7 +22,7 @@
  *   expert index, bf16 activations/weights and int4 blocks of 32 with an fp16
  *   scale.
  *
- * Readings taken where the pages are silent (each also listed in the design notes):
+ * Readings taken where the pages are silent:
  *   R1  logits: l[t][e] = fp32(S) with S the fp64 sum of the exact products
  *       x[t][h]*Wr[e][h] in "wave-64 order": 64 partial sums P_j = sum over i of
  *       prod[j + 64 i] (i ascending), then P_j += P_{j+32}, +16, +8, +4, +2, +1;
