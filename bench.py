@@ -314,7 +314,7 @@ def bench_stack(torch, moe, synth, shape, steps, warmup, use_graph, name, steere
     place; timed plain and with the first `steered` layers steered (the pages
     steer 41 layers without naming them)."""
     Ls = synth.STACK_INT4_LAYERS
-    log(f"[{name}] generating {Ls} int4 layers")
+    log(f"[{name}] generating {Ls} {shape.wdt} layers")
     layers = [synth.make_device_layer(shape, seed=0, cfg=5, layer=l, device="cuda") for l in range(Ls)]
     vs = [torch.from_numpy(synth.steer_vector(shape.H, layer=l)).cuda() if l < steered else None for l in range(Ls)]
     x0 = layers[0].x
