@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ lo
 // is never a candidate; NaN rows are unspecified, as in routing).
 constexpr int THR_MAX = 64;
 constexpr int FR_RING = 2;
-template <int VPL>
+template <int VPL, bool FULL>
 __global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict__ logits, int64_t T, int E, int K,
                                                         int64_t rows_per_layer_blocks,
                                                         unsigned long long* __restrict__ counts) {
@@ -101,32 +101,31 @@ __global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict_
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
             const int e = l + j * WAVE;
-            v[j] = __builtin_nontemporal_load(r + (e < E ? e : E - 1));
+            v[j] = __builtin_nontemporal_load(r + (FULL || e < E ? e : E - 1));
         }
     };
     bool have = false;        // wave-uniform threshold state
     float th = 0.f, th_step = 0.f;
     auto process = [&](const float (&cur)[VPL]) __attribute__((always_inline)) {
-        auto valid = [&](int j) __attribute__((always_inline)) { return l + j * WAVE < E; };
+        auto valid = [&](int j) __attribute__((always_inline)) { return FULL || l + j * WAVE < E; };
+        // one pass: count the values at or above th and compact the first
+        // THR_MAX of them (used only when the count lands in [K, THR_MAX])
         int c = 0;
         if (have) {
-#pragma unroll
-            for (int j = 0; j < VPL; j++) c += __popcll(__ballot(valid(j) && cur[j] >= th));
-        }
-        c = __builtin_amdgcn_readfirstlane(c);
-        if (have && c >= K && c <= THR_MAX) {
-            int pos0 = 0;
 #pragma unroll
             for (int j = 0; j < VPL; j++) {
                 const bool in = valid(j) && cur[j] >= th;
                 const unsigned long long m = __ballot(in);
-                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                if (in) {
-                    cval[pos0 + below] = cur[j];
-                    cid[pos0 + below] = l + j * WAVE;
+                const int p = c + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (in && p < THR_MAX) {
+                    cval[p] = cur[j];
+                    cid[p] = l + j * WAVE;
                 }
-                pos0 += __popcll(m);
+                c += __popcll(m);
             }
+        }
+        c = __builtin_amdgcn_readfirstlane(c);
+        if (have && c >= K && c <= THR_MAX) {
             __builtin_amdgcn_wave_barrier();
             // slot l's composite: order key (the float order of non-NaN values,
             // -0 == +0), then the lower slot (= lower expert); 0 past c
@@ -136,10 +135,13 @@ __global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict_
             comp[l] = mine;
             __builtin_amdgcn_wave_barrier();
             int rank = 0;
-            for (int j = 0; j < c; j += 2) {
+            for (int j = 0; j < c; j += 4) {
                 const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(comp + j);   // the same 16 B for every lane
+                const ulonglong2 r = *reinterpret_cast<const ulonglong2*>(comp + j + 2);
                 rank += q.x > mine ? 1 : 0;
                 rank += q.y > mine ? 1 : 0;
+                rank += r.x > mine ? 1 : 0;
+                rank += r.y > mine ? 1 : 0;
             }
             if (l < c && rank < K) atomicAdd(&hist[me], 1);
             if (c < K + 3) th -= th_step;
@@ -224,7 +226,12 @@ static void count_dispatch(const float* logits, int L, int64_t T, int E, int K, 
     if constexpr (VPL >= 4 && VPL <= 16) {
         if (K <= THR_MAX) {
             const size_t lds = (size_t)4 * THR_MAX * 16 + (size_t)E * sizeof(int);
-            hipLaunchKernelGGL(k_freq_count_thr<VPL>, grid, dim3(256), lds, st, logits, T, E, K, blocks, counts);
+            if (E == VPL * WAVE)
+                hipLaunchKernelGGL((k_freq_count_thr<VPL, true>), grid, dim3(256), lds, st, logits, T, E, K, blocks,
+                                   counts);
+            else
+                hipLaunchKernelGGL((k_freq_count_thr<VPL, false>), grid, dim3(256), lds, st, logits, T, E, K, blocks,
+                                   counts);
             return;
         }
     }
