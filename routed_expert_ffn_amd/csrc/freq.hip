@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ lo
 // threshold only decides which exact method runs, never the result (a NaN
 // is never a candidate; NaN rows are unspecified, as in routing).
 constexpr int THR_MAX = 64;
-constexpr int FR_RING = 2;
+constexpr int FR_RING = 3;
 template <int VPL, bool FULL>
 __global__ __launch_bounds__(256) void k_freq_count_thr(const float* __restrict__ logits, int64_t T, int E, int K,
                                                         int64_t rows_per_layer_blocks,
