@@ -109,6 +109,13 @@ def test_permute_ffn_combine_freq_reject_bad_arguments(L):
                    None) == moe.MOE_ERR_INVALID_ARG              # scales required
     assert L.moe_combine(FAKE, moe.BF16, FAKE, FAKE, None, 5, 10, 2044, FAKE, moe.BF16, None) == \
         moe.MOE_ERR_UNSUPPORTED                                  # H % 8
+    st = L.moe_combine_steer
+    assert st(FAKE, moe.BF16, FAKE, FAKE, None, None, 5, 10, 2048, FAKE, moe.BF16, None) == \
+        moe.MOE_ERR_INVALID_ARG                                  # the direction is required
+    assert st(FAKE, moe.BF16, FAKE, FAKE, None, FAKE, 5, 10, 8200, FAKE, moe.BF16, None) == \
+        moe.MOE_ERR_UNSUPPORTED                                  # one row per block: H <= 8192
+    assert st(FAKE, moe.BF16, FAKE, FAKE, None, ctypes.c_void_p(0x10004), 5, 10, 2048, FAKE, moe.BF16, None) == \
+        moe.MOE_ERR_UNSUPPORTED                                  # misaligned direction
     assert L.moe_combine(None, moe.BF16, FAKE, FAKE, None, 5, 10, 2048, FAKE, moe.BF16, None) == \
         moe.MOE_ERR_INVALID_ARG
     assert L.moe_combine(FAKE, moe.BF16, FAKE, FAKE, ctypes.c_void_p(0x10004), 5, 10, 2048, FAKE, moe.BF16, None) == \

@@ -285,6 +285,28 @@ def test_combine_steer_matches_oracle(ydt, odt, T, K, H, with_res):
     assert along.max() <= (1e-5 if odt == "f32" else 2e-2)
 
 
+def test_combine_steer_prefill_shape_sampled_rows():
+    """The steered combine at the prefill chunk's shape (8192 tokens, K 10, H 2048,
+    bf16), the launch the benchmark times: sampled rows against the oracle."""
+    from oracle import steer
+    T, K, H = 8192, 10, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    y = torch.randn((T * K, H), generator=g, device="cuda").to(torch.bfloat16)
+    inv = torch.randperm(T * K, generator=g, device="cuda").to(torch.int32)
+    w = torch.rand((T, K), generator=g, device="cuda")
+    res = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.from_numpy(synth.steer_vector(H, seed=5)).cuda()
+    out = moe.combine(y, inv, w, residual=res, steer_v=v)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(4).choice(T, 30, replace=False)]))
+    inv_h, w_h = to_host(inv).reshape(T, K), to_host(w)
+    y_rows = as_f64(to_host(y[torch.from_numpy(inv_h[rows].reshape(-1).astype(np.int64)).cuda()]))
+    ref = steer.combine_steer(y_rows, np.arange(len(rows) * K), w_h[rows], to_host(v).astype(np.float64),
+                              as_f64(to_host(res))[rows])
+    assert row_rel_err(to_host(out)[rows], ref) <= TOL_BF16
+
+
 def test_combine_steer_in_place_and_unit_axis():
     """out aliasing residual gives the same bytes; v = e_j zeroes column j exactly
     and leaves every other column as the plain combine rounds it."""
