@@ -17,6 +17,12 @@
 //   while staging the tile into LDS: d*q is exact in fp32 and is rounded to
 //   bf16 for the MFMA (relative weight error <= 2^-9).
 // fp32 activations and weights: plain per-element kernels (fp32 FMA).
+//
+// launch_ffn picks the path: int3 / int2 weights go to the few-token streaming
+// kernels (ffn_stream.hip); T <= 16 to the small-T paths (ffn_small.hip, which
+// hands T <= 8 bf16 and int4 shapes on to the streaming kernels); bf16 and
+// int4 at larger T to the grouped GEMM (ffn_gemm.hip) where its shapes allow;
+// anything else to the two MFMA kernels here.
 #include "common.h"
 #include "launch.h"
 

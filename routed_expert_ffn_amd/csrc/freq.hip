@@ -7,11 +7,12 @@
 // 而不伤脑的"; the per-(layer, expert) ranking of the kwkr.cn Coder write-up,
 // "专家配置文件：48 x 256 的全量排名").
 //
-//   k_freq_count  top-K of every logit row (routing's rule: larger first, ties
-//                 to the lower id), per-block LDS histogram, int64 totals via
-//                 integer atomics (exact and order-independent).  Wide rows
-//                 take a threshold pass first (below); narrow ones, and rows
-//                 the threshold does not settle, use routing's wave selection.
+//   k_freq_count      top-K of every logit row (routing's rule: larger first,
+//                     ties to the lower id), per-block LDS histogram, int64
+//                     totals via integer atomics (exact and order-independent).
+//   k_freq_count_thr  the same counts for wide rows (E > 128): a threshold cut
+//                     settles almost every row (below); the rest use routing's
+//                     wave selection, as k_freq_count does for every row.
 //   k_freq_rank   per layer: rank_of[e] = number of experts ahead of e in
 //                 (count desc, id asc) order; keep_map = ids of rank < keep in
 //                 ascending id order.
@@ -67,9 +68,12 @@ __global__ __launch_bounds__(256) void k_freq_count(const float* __restrict__ lo
 // before it (all rows of a wave belong to one layer).  If c, the number of
 // values >= th, lies in [K, 64], every winner is among those c candidates
 // (the K-th largest value is >= th), so they are packed into one slot per
-// lane in expert order, and each candidate's rank is the number of others
-// with a larger (order key, lower slot) pair -- one 64-bit compare per
-// candidate, no branches.  The K candidates of rank < K are the winners.
+// lane in expert order (the count and the packing share one ballot per
+// compare), and each candidate's rank is the number of others with a larger
+// (order key, lower slot) pair -- one 64-bit compare per candidate, four per
+// LDS read, no branches.  The K candidates of rank < K are the winners.  The
+// row work is vector-ALU bound, so FULL (E = 64 * VPL) drops the per-slot
+// bounds checks and three rows are in flight per wave.
 // Any other row takes routing's selection, whose K-th and first values then
 // reset th (the K-th value minus 3/4 of their spread) and its adjustment
 // step; after a cut row th moves by the step to keep c within [K + 3, 28].  The
