@@ -121,6 +121,22 @@ def test_small_layers_span_tiles(s):
 
 
 @pytest.mark.parametrize("wdt", ["bf16", "int4"])
+@pytest.mark.parametrize("T", [8, 9, 16, 17, 63, 65])
+def test_path_boundaries(T, wdt):
+    """Token counts on both sides of every path switch (streaming kernels up to
+    8 tokens, the small-T kernels up to 16, the grouped GEMM above; the exact
+    router below 64 tokens, the estimate with rechecks from 64)."""
+    s = synth.LayerShape(T=T, H=1024, E=24, K=4, F=512, act="bf16", wdt=wdt, zipf=True)
+    h = synth.make_host_layer(s, seed=11, cfg=8)
+    d = device_from_host(h)
+    ref_idx, ref_w, _ = oracle.route(h.x, h.wr, s.K, h.bias)
+    out, r = run_layer(d)
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    ref_out = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d))
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "int4"])
 def test_gemm_path_blocks_walk_several_items(wdt):
     """More 128-row tiles than the chip holds blocks: every persistent block of
     the grouped GEMM handles several (expert, tile) items in turn (bf16: 128 x
