@@ -164,6 +164,10 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
     y = lw.y
     ws_r, ws_p, ws_f = lw.route_ws, lw.perm_ws, lw.ffn_ws
 
+    def calls_route_group():
+        for L in layers:
+            moe.route_group(L.x, L.wr, shape.K, bias=L.bias, workspace=lw.group_ws, out=lw.route_out + lw.perm_out)
+
     def calls_route():
         for L in layers:
             moe.route(L.x, L.wr, shape.K, bias=L.bias, workspace=ws_r, out=lw.route_out)
@@ -187,20 +191,22 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
             moe.combine(y, p["inv"], p["w"], out=lw.out, steer_v=v)
 
     parts = {}
-    for pname, f in (("route", calls_route), ("permute", calls_permute), ("ffn", calls_ffn),
-                     ("combine", calls_combine), ("combine_steer", calls_combine_steer)):
+    for pname, f in (("route_group", calls_route_group), ("ffn", calls_ffn), ("combine", calls_combine),
+                     ("route", calls_route), ("permute", calls_permute), ("combine_steer", calls_combine_steer)):
         gf = capture(torch, f).replay if use_graph else f
         timer.run(gf, wreps)
         t, _ = timer.run(gf, reps)
         parts[pname] = t / n_steps * 1e6
     steer_us = parts.pop("combine_steer")
+    # the step runs routing and grouping as one call; the separate calls are kept for reference
+    separate = {"route": parts.pop("route"), "permute": parts.pop("permute")}
     b_step = sum(a["b_step"] for a in acct) / len(acct)
     b_ffn = sum(a["b_ffn"] for a in acct) / len(acct)
     f_ffn = acct[0]["f_ffn"]
     f_all = acct[0]["f_ffn"] + acct[0]["f_router"]
     touched = sum(a["touched"] for a in acct) / len(acct)
     res = dict(name=name, T=shape.T, ms_per_step=ms, value=shape.T / (ms / 1e3), steps=n_steps, warmup=wreps * sets,
-               wall_s=wall, parts_us=parts, combine_steer_us=steer_us, touched_experts=touched, bytes_per_step=b_step, bytes_ffn=b_ffn,
+               wall_s=wall, parts_us=parts, separate_calls_us=separate, combine_steer_us=steer_us, touched_experts=touched, bytes_per_step=b_step, bytes_ffn=b_ffn,
                flops_ffn=f_ffn, flops_step=f_all,
                hbm_frac_step=b_step / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
                mfma_frac_step=f_all / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
@@ -472,6 +478,7 @@ def main():
         else main_res.get("roofline"),
         "cpu_baseline": cpu,
         "step_breakdown_us": {k: round(v, 2) for k, v in main_res.get("parts_us", {}).items()},
+        "separate_calls_us": {k: round(v, 2) for k, v in main_res.get("separate_calls_us", {}).items()},
         "step_hbm_frac": round(main_res.get("hbm_frac_step", 0.0), 4),
         "also": also,
     }

@@ -141,6 +141,19 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                        void* workspace, size_t ws_bytes, moe_stream stream);
 
+/* ---------------------------------------------------------------- routing + grouping
+ * moe_route followed by moe_permute on its topk_idx, with the same results
+ * (no logits_out).  For a few tokens on the exact path (T <= 16, T*K <= 1024,
+ * T < 64 or fp32 activations) the selection and the grouping run in one
+ * launch after the logits; otherwise the two calls run as they are.
+ * Workspace: moe_route_group_workspace_size(T, H, E, K, x_dtype) bytes. */
+size_t moe_route_group_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype);
+moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router, const float* bias,
+                           int32_t T, int32_t H, int32_t E, int32_t K,
+                           int32_t* topk_idx, float* topk_w,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                           void* workspace, size_t ws_bytes, moe_stream stream);
+
 /* ---------------------------------------------------------------- experts
  * Grouped SwiGLU expert FFN (page 1 §3: gate, up and down per expert).  For
  * every permuted row p in expert e's segment [offsets[e], offsets[e+1]), with

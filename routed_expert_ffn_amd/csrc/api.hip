@@ -67,14 +67,27 @@ size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int3
     return route_ws_layout(T, H, E, x_dtype).total;
 }
 
-moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T, int32_t H,
-                     int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
-                     size_t ws_bytes, moe_stream stream) {
+}  // extern "C"
+
+namespace {
+moe_status route_check(const void* x, int32_t x_dtype, const float* w_router, int32_t T, int32_t H, int32_t E,
+                       int32_t K, const int32_t* topk_idx, const float* topk_w) {
     if (T < 0 || H <= 0 || E <= 0 || K <= 0 || K > E) return MOE_ERR_INVALID_ARG;
     if (!w_router || (T > 0 && (!x || !topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
     if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if ((int64_t)T * K > INT32_MAX || (int64_t)T * E > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
     if (K > MAX_K || E > MAX_E || H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T, int32_t H,
+                     int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
+                     size_t ws_bytes, moe_stream stream) {
+    const moe_status chk = route_check(x, x_dtype, w_router, T, H, E, K, topk_idx, topk_w);
+    if (chk != MOE_OK) return chk;
     const size_t need = moe_route_workspace_size(T, H, E, K, x_dtype);
     if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
@@ -120,6 +133,34 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
     if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
     return hip_status(launch_permute(topk_idx, T * K, E, counts, offsets, perm, inv_perm, (int32_t*)workspace,
                                      S(stream)));
+}
+
+size_t moe_route_group_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype) {
+    if (T < 0 || E <= 0 || H <= 0 || K <= 0) return 0;
+    return round256(moe_route_workspace_size(T, H, E, K, x_dtype)) + moe_permute_workspace_size(T, K, E);
+}
+
+moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T,
+                           int32_t H, int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes,
+                           moe_stream stream) {
+    const moe_status chk = route_check(x, x_dtype, w_router, T, H, E, K, topk_idx, topk_w);
+    if (chk != MOE_OK) return chk;
+    if (!counts || !offsets || (T > 0 && (!perm || !inv_perm))) return MOE_ERR_INVALID_ARG;
+    const size_t rws = round256(moe_route_workspace_size(T, H, E, K, x_dtype));
+    if (!workspace || ws_bytes < moe_route_group_workspace_size(T, H, E, K, x_dtype)) return MOE_ERR_WORKSPACE;
+    if (T > 0 && !fast_route_eligible(T, H, E, x_dtype, x, w_router, nullptr) && route_group_fused_eligible(T, K, E)) {
+        hipStream_t st = S(stream);
+        float* lg = (float*)workspace;
+        hipError_t err = launch_logits_exact(x, x_dtype == MOE_BF16, w_router, bias, T, H, E, lg, st);
+        if (err != hipSuccess) return MOE_ERR_HIP;
+        return hip_status(launch_route_select_group(lg, T, E, K, topk_idx, topk_w, counts, offsets, perm, inv_perm, st));
+    }
+    const moe_status r = moe_route(x, x_dtype, w_router, bias, T, H, E, K, topk_idx, topk_w, nullptr, workspace, rws,
+                                   stream);
+    if (r != MOE_OK) return r;
+    return moe_permute(topk_idx, T, K, E, counts, offsets, perm, inv_perm, (char*)workspace + rws, ws_bytes - rws,
+                       stream);
 }
 
 size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_t F, int32_t x_dtype,

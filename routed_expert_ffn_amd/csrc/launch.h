@@ -18,6 +18,10 @@ hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* b
 hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
                                int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
                                int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st);
+// A few tokens on exact logits: selection and grouping in one launch (route.hip)
+bool route_group_fused_eligible(int T, int K, int E);
+hipError_t launch_route_select_group(const float* logits, int T, int E, int K, int32_t* idx, float* w,
+                                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t st);
 
 // permute.hip
 constexpr int PERM_CHUNK = 1024;   // slots per grouping block

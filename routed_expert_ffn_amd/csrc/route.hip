@@ -25,6 +25,7 @@
 // them or let an outside expert in); any other token recomputes the exact
 // logits of every expert within tau of its K-th value and selects among those.
 #include "common.h"
+#include "group.h"
 #include "launch.h"
 
 // ------------------------------------------------------------------ exact logits
@@ -419,6 +420,55 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     write_selection(sel_v, sel_i, K, t, idx_out, w_out);
 }
 
+// A few tokens on exact logits (T <= 16, T*K <= PERM_CHUNK): one block
+// selects every token's top K (one wave per token, as k_route_select) and then
+// groups the T*K slots by expert in the same block -- counts, offsets, the
+// stable permutation and its inverse, exactly as the grouping kernels do -- so
+// selection and grouping take one launch.
+template <int VPL>
+__global__ __launch_bounds__(1024) void k_route_select_group(const float* __restrict__ logits, int T, int E, int K,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);   // [E]
+    int* cur = reinterpret_cast<int*>(mask + E);                              // [E]
+    int* sidx = cur + E;                                                      // [T*K] selected experts
+    __shared__ int wave_tot[16];
+    const int wave = threadIdx.x / WAVE, l = lane_id();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) { cur[e] = 0; mask[e] = 0ull; }
+    if (wave < T) {
+        const int t = wave;
+        const float* row = logits + (long)t * E;
+        uint32_t kv[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; j++) {
+            const int e = l + j * WAVE;
+            kv[j] = e < E ? f32_order_key(row[e]) : 0u;
+        }
+        uint32_t key;
+        int sel_i;
+        select_top<VPL>(kv, K, key, sel_i);
+        write_selection(order_key_value(key), sel_i, K, t, idx_out, w_out);
+        if (l < K) sidx[t * K + l] = sel_i;
+    }
+    __syncthreads();
+    const int n = T * K;
+    for (int s = threadIdx.x; s < n; s += blockDim.x) {
+        const int e = sidx[s];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cur[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = cur[e];
+    __syncthreads();
+    const int total = block_exclusive_scan(cur, E, wave_tot);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = cur[e];
+    if (threadIdx.x == 0) offsets[E] = total;
+    __syncthreads();
+    if (wave == 0) wave_stable_scatter(sidx, 0, n, E, cur, mask, perm, inv);
+}
+
 // Re-decision of the queued tokens on exact logits, one block per token at a
 // time: the candidates are every expert whose estimate exceeds the cut (all E
 // if more than 64 do), their exact keys are computed four per wave pass, and
@@ -623,4 +673,27 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, float t
     if (vpl <= 32) MOE_SEL(32);
     MOE_SEL(64);
 #undef MOE_SEL
+}
+
+bool route_group_fused_eligible(int T, int K, int E) {
+    return T >= 1 && T <= 16 && (long)T * K <= PERM_CHUNK && E <= 4096;
+}
+
+hipError_t launch_route_select_group(const float* logits, int T, int E, int K, int32_t* idx, float* w,
+                                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t st) {
+    const size_t lds = (size_t)E * (sizeof(unsigned long long) + sizeof(int)) + (size_t)T * K * sizeof(int);
+    const dim3 block(WAVE * (T > 4 ? T : 4));
+    const int vpl = (E + WAVE - 1) / WAVE;
+#define MOE_SELG(V)                                                                                              \
+    hipLaunchKernelGGL((k_route_select_group<V>), dim3(1), block, lds, st, logits, T, E, K, idx, w, counts, offsets, \
+                       perm, inv);                                                                               \
+    return hipGetLastError()
+    if (vpl <= 1) { MOE_SELG(1); }
+    if (vpl <= 2) { MOE_SELG(2); }
+    if (vpl <= 4) { MOE_SELG(4); }
+    if (vpl <= 8) { MOE_SELG(8); }
+    if (vpl <= 16) { MOE_SELG(16); }
+    if (vpl <= 32) { MOE_SELG(32); }
+    MOE_SELG(64);
+#undef MOE_SELG
 }

@@ -19,7 +19,7 @@ _QUANT_BY_BITS = {4: INT4_B32, 3: INT3_B32, 2: INT2_B32}
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_ffn_workspace_size", "moe_ffn",
-           "moe_combine", "moe_combine_steer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
+           "moe_route_group_workspace_size", "moe_route_group", "moe_combine", "moe_combine_steer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
            "moe_profile_hits", "moe_strp_size", "moe_strp_write", "moe_strp_read", "moe_profile_remap"]
 
 
@@ -71,6 +71,10 @@ def load():
                           vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp]
+    L.moe_route_group_workspace_size.restype = sz
+    L.moe_route_group_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.moe_route_group.restype = ctypes.c_int
+    L.moe_route_group.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_combine_steer.restype = ctypes.c_int
     L.moe_combine_steer.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp]
     L.moe_expert_freq.restype = ctypes.c_int
@@ -197,6 +201,41 @@ def permute(topk_idx, E: int, workspace=None, stream=None, out=None):
     _chk(load().moe_permute(_ptr(topk_idx), T, K, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws),
                             nb, _stream(stream)), "moe_permute")
     return counts, offsets, perm, inv
+
+
+# ------------------------------------------------------------------ moe_route_group
+def route_group_workspace_size(T, H, E, K, x_dtype=BF16) -> int:
+    return int(load().moe_route_group_workspace_size(T, H, E, K, x_dtype))
+
+
+def route_group(x, w_router, K: int, bias=None, workspace=None, stream=None, out=None):
+    """moe_route then moe_permute in one call (one launch for selection and
+    grouping when few tokens are routed).  Returns (idx, w, counts, offsets,
+    perm, inv); out: optional 6-tuple to fill."""
+    _need(x, "x")
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(w_router, "w_router", torch.float32, (E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    dev = x.device
+    if out is not None:
+        idx, w, counts, offsets, perm, inv = out
+        for n, t, dt, shp in (("topk_idx", idx, torch.int32, (T, K)), ("topk_w", w, torch.float32, (T, K)),
+                              ("counts", counts, torch.int32, (E,)), ("offsets", offsets, torch.int32, (E + 1,)),
+                              ("perm", perm, torch.int32, (T * K,)), ("inv_perm", inv, torch.int32, (T * K,))):
+            _need(t, n, dt, shp)
+    else:
+        i32 = dict(dtype=torch.int32, device=dev)
+        idx, w = torch.empty((T, K), **i32), torch.empty((T, K), dtype=torch.float32, device=dev)
+        counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+        perm, inv = torch.empty(T * K, **i32), torch.empty(T * K, **i32)
+    nb = route_group_workspace_size(T, H, E, K, _act_dtype(x))
+    ws = _workspace(nb, dev, workspace)
+    _chk(load().moe_route_group(_ptr(x), _act_dtype(x), _ptr(w_router), _ptr(bias), T, H, E, K, _ptr(idx), _ptr(w),
+                                _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws), nb, _stream(stream)),
+         "moe_route_group")
+    return idx, w, counts, offsets, perm, inv
 
 
 # ------------------------------------------------------------------ moe_ffn
@@ -371,6 +410,7 @@ class LayerWorkspace:
         xd = F32 if x_dtype == torch.float32 else BF16
         self.y_dtype = y_dtype or x_dtype
         self.route_ws = torch.empty(route_workspace_size(T, H, E, K, xd), dtype=torch.uint8, device=device)
+        self.group_ws = torch.empty(route_group_workspace_size(T, H, E, K, xd), dtype=torch.uint8, device=device)
         self.perm_ws = torch.empty(permute_workspace_size(T, K, E), dtype=torch.uint8, device=device)
         self.ffn_ws = torch.empty(ffn_workspace_size(T, K, E, H, F, xd, w_dtype), dtype=torch.uint8, device=device)
         self.y = torch.empty((T * K, H), dtype=self.y_dtype, device=device)
@@ -383,14 +423,13 @@ class LayerWorkspace:
 
 def layer(x, w_router, wg, wu, wd, K: int, bias=None, sg=None, su=None, sd=None, residual=None, lw=None,
           stream=None, out=None, steer_v=None):
-    """route -> permute -> ffn -> combine (steered if steer_v is given) for one
-    MoE layer.  Returns (out, routing dict)."""
+    """route + permute (one call, moe_route_group) -> ffn -> combine (steered
+    if steer_v is given) for one MoE layer.  Returns (out, routing dict)."""
     T, H = x.shape
     E, F = wg.shape[0], wg.shape[1]
-    idx, w = route(x, w_router, K, bias=bias, workspace=lw.route_ws if lw else None, stream=stream,
-                   out=lw.route_out if lw else None)
-    counts, offsets, perm, inv = permute(idx, E, workspace=lw.perm_ws if lw else None, stream=stream,
-                                         out=lw.perm_out if lw else None)
+    idx, w, counts, offsets, perm, inv = route_group(
+        x, w_router, K, bias=bias, workspace=lw.group_ws if lw else None, stream=stream,
+        out=(lw.route_out + lw.perm_out) if lw else None)
     y = ffn(x, wg, wu, wd, offsets, perm, K, sg, su, sd, y_dtype=lw.y_dtype if lw else None,
             out=lw.y if lw else None, workspace=lw.ffn_ws if lw else None, stream=stream)
     if out is None and lw is not None:

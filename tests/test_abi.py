@@ -109,6 +109,15 @@ def test_permute_ffn_combine_freq_reject_bad_arguments(L):
                    None) == moe.MOE_ERR_INVALID_ARG              # scales required
     assert L.moe_combine(FAKE, moe.BF16, FAKE, FAKE, None, 5, 10, 2044, FAKE, moe.BF16, None) == \
         moe.MOE_ERR_UNSUPPORTED                                  # H % 8
+    rg = L.moe_route_group
+    nrg = moe.route_group_workspace_size(5, 2048, 512, 10, moe.BF16)
+    assert nrg >= moe.route_workspace_size(5, 2048, 512, 10, moe.BF16) + moe.permute_workspace_size(5, 10, 512)
+    assert rg(FAKE, moe.BF16, FAKE, None, 5, 2048, 512, 10, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, nrg, None) == \
+        moe.MOE_ERR_INVALID_ARG                                  # counts required
+    assert rg(FAKE, moe.BF16, FAKE, None, 5, 2048, 512, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nrg - 1,
+              None) == moe.MOE_ERR_WORKSPACE
+    assert rg(FAKE, moe.BF16, FAKE, None, 5, 2048, 512, 33, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nrg, None) == \
+        moe.MOE_ERR_UNSUPPORTED                                  # K > 32
     st = L.moe_combine_steer
     assert st(FAKE, moe.BF16, FAKE, FAKE, None, None, 5, 10, 2048, FAKE, moe.BF16, None) == \
         moe.MOE_ERR_INVALID_ARG                                  # the direction is required

@@ -251,6 +251,43 @@ def test_permute_matches_stable_counting_sort(T, K, E, mode):
         assert torch.equal(g, a)
 
 
+# ---------------------------------------------------------------- routing + grouping in one call
+@pytest.mark.parametrize("T,E,K,H,act,ties", [
+    (1, 512, 10, 2048, "bf16", False),
+    (5, 512, 10, 2048, "bf16", True),       # the verify step, with tied router rows
+    (16, 64, 32, 256, "bf16", True),        # 512 slots
+    (16, 4096, 4, 256, "f32", False),       # the widest expert count
+    (3, 300, 10, 512, "bf16", True),        # experts not a multiple of 64
+    (17, 64, 8, 256, "bf16", False),        # past the one-block path: route, then permute
+    (100, 512, 10, 2048, "bf16", False),    # the estimate path, then permute
+    (0, 64, 4, 256, "bf16", False),
+])
+def test_route_group_matches_oracle_and_separate_calls(T, E, K, H, act, ties):
+    rng = np.random.default_rng(T * 7 + E)
+    x32 = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    if ties:
+        wr[E // 2] = wr[1]                     # equal logits on two experts: the lower id must win
+        wr[E - 1] = wr[0]
+    x_h = synth.f32_to_bf16_bits(x32) if act == "bf16" else x32
+    x = (torch.from_numpy(x_h.view(np.int16)).cuda().view(torch.bfloat16) if act == "bf16"
+         else torch.from_numpy(x_h).cuda())
+    wr_d = torch.from_numpy(wr).cuda()
+    got = moe.route_group(x, wr_d, K)
+    idx2, w2 = moe.route(x, wr_d, K)
+    sep = moe.permute(idx2, E)
+    torch.cuda.synchronize()
+    names = ("idx", "w", "counts", "offsets", "perm", "inv")
+    r = dict(zip(names, got))
+    for a, b in zip(got, (idx2, w2) + tuple(sep)):
+        assert torch.equal(a, b), "one call and two calls must agree bit for bit"
+    if T == 0:
+        assert not r["counts"].any() and not r["offsets"].any()
+        return
+    ref_idx, ref_w, _ = oracle.route(x_h, wr, K)
+    check_routing_and_grouping(r, ref_idx, ref_w, E)
+
+
 # ---------------------------------------------------------------- combine
 def test_combine_in_place_residual_and_fp32():
     rng = np.random.default_rng(5)
