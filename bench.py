@@ -1,17 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-One step = one pass of the whole hot path (route -> permute -> ffn ->
-combine) over one batch of synthetic input.  The headline workload is the
-speculative verify step: 5 tokens (4 drafted + 1, the pages' `--spec 4`),
+One step = one pass of the whole hot path (route + permute in one call ->
+ffn -> combine) over one batch of synthetic input.  The headline workload is
+the speculative verify step: 5 tokens (4 drafted + 1, the pages' `--spec 4`),
 hidden 2048, 512 experts, top-10, expert width 512, bf16 weights, fp32 router.
-Further workloads (the 8192-token prefill chunk, the pruning statistic over
-48 x 262144 x 512 logits, the pruned 48-layer int4 stack) are reported under
-"also".
+Further workloads are reported under "also": the 8192-token prefill chunk, the
+pruning statistic over 48 x 262144 x 512 logits with the expert profile built
+from it, the pruned 48-layer int4 stack (plain and with 41 steered layers),
+and the verify layer and stack with int4 / int3 / int2 experts.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workloads verify,prefill,freq,stack,copy]
+    python bench.py [--steps K] [--warmup W]
+                    [--workloads verify,prefill,freq,stack,lowbit,copy]
 """
 from __future__ import annotations
 
