@@ -47,3 +47,54 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         "-q", "-x", "-p", "no:cacheprovider"], env=env, cwd=ROOT, capture_output=True, text=True)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+# The numpy half of the oracle (expert profile and steering projection): each
+# mistake goes into a copy of the oracle package, and the pins of those parts
+# run against the copy from a scratch tree that mirrors the repository.
+PY_MUTANTS = {
+    "steer_sign": ("steer.py", "return h - np.multiply.outer(h @ v, v)", "return h + np.multiply.outer(h @ v, v)"),
+    "steer_slot_major_inverse": ("steer.py", "inv = np.asarray(inv).reshape(T, K)", "inv = np.asarray(inv).reshape(K, T).T"),
+    "steer_residual_dropped": ("steer.py", "if residual is not None:", "if False:"),
+    "profile_ties_to_higher_index": ("profile.py", "(-int(flat[i]), i)", "(-int(flat[i]), -i)"),
+    "profile_hits_one_pair_too_many": ("profile.py", "np.asarray(pairs)[:S]", "np.asarray(pairs)[:S + 1]"),
+    "profile_remap_keeps_pruned": ("profile.py", "j = new_index[l].get(e)", "j = new_index[l].get(e, e)"),
+    "profile_inverse_off_by_one": ("profile.py", "inv[l, e] = r", "inv[l, e] = r + 1"),
+    "strp_pair_fields_swapped": ("profile.py", 'struct.pack("<HH", l, e)', 'struct.pack("<HH", e, l)'),
+}
+PY_PINS = "profile or strp or steer"
+
+
+def _run_py_pins(tmp_path, mutant):
+    import shutil
+    import oracle
+    oracle.build()
+    tree = tmp_path / "tree"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tree / "oracle", ignore=shutil.ignore_patterns("_build", "__pycache__"))
+    (tree / "tests").mkdir()
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tree / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tree / "tests" / "golden")
+    os.symlink(os.path.join(ROOT, "routed_expert_ffn_amd"), tree / "routed_expert_ffn_amd")
+    if mutant is not None:
+        fname, a, b = mutant
+        p = tree / "oracle" / fname
+        src = p.read_text()
+        assert src.count(a) == 1, f"mutation anchor {a!r} not found exactly once in {fname}"
+        p.write_text(src.replace(a, b))
+    env = dict(os.environ, MOE_ORACLE_LIB_OVERRIDE=oracle.LIB)
+    return subprocess.run([sys.executable, "-m", "pytest", str(tree / "tests" / "test_oracle_pins.py"), "-q", "-x",
+                           "-k", PY_PINS, "-p", "no:cacheprovider"], env=env, cwd=str(tree),
+                          capture_output=True, text=True)
+
+
+def test_python_pins_pass_on_the_unmutated_copy(tmp_path):
+    r = _run_py_pins(tmp_path, None)
+    assert r.returncode == 0 and " passed" in r.stdout, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_python_pins_catch_planted_mistake(name, tmp_path):
+    r = _run_py_pins(tmp_path, PY_MUTANTS[name])
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+    assert " failed" in r.stdout, r.stdout[-2000:]   # a failing pin, not a broken copy
