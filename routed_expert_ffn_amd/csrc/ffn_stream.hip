@@ -25,6 +25,8 @@
 //     combined across the wave by a transposing butterfly (with V sums per
 //     lane, each xor step keeps half of them and adds the partner's copy of
 //     that half, so lane l ends with the full sum of entry l >> (6 - log2 V)).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -77,6 +79,18 @@ MOE_DEV float wave_tr_reduce(float (&v)[V]) {
 template <int V>
 constexpr int tr_shift() { return V == 64 ? 0 : V == 32 ? 1 : V == 16 ? 2 : V == 8 ? 3 : V == 4 ? 4 : V == 2 ? 5 : 6; }
 
+// Calls f(std::integral_constant<int, R>) with R = the expert's row count n
+// rounded up to 1, 2, 4 or NT: the accumulators and the cross-lane reduction
+// are sized for the rows an item really has (at T = 5 almost every expert
+// has one), not for the largest T the kernel accepts.  n is wave-uniform.
+template <int NT, typename Fn>
+MOE_DEV void by_rows(int n, Fn&& f) {
+    if (n <= 1) f(std::integral_constant<int, 1>{});
+    else if (n <= 2) f(std::integral_constant<int, (NT < 2 ? NT : 2)>{});
+    else if (n <= 4) f(std::integral_constant<int, (NT < 4 ? NT : 4)>{});
+    else f(std::integral_constant<int, NT>{});
+}
+
 // The touched experts (count > 0) in expert order as (expert, first row,
 // rows), built by the whole block from the grouping offsets; returns their
 // number.  Needs 256 threads and E <= 256 * EPT.
@@ -126,10 +140,13 @@ MOE_DEV void stage_lds(const void* src, int n_kb, unsigned char* lds, int wave, 
 // the load of the item RING-1 steps ahead is issued before each multiply, so
 // RING-1 items' weights are always in flight.  Loads past the end repeat the
 // last item (never predicated); all have landed when the walk returns.
-template <int RING, typename Buf, typename LoadF, typename ComputeF>
-MOE_DEV void ring_walk(int it, int W, int n, Buf (&buf)[RING], LoadF&& load, ComputeF&& compute) {
+template <int RING, typename Buf, typename LoadF>
+MOE_DEV void ring_start(int it, int W, int n, Buf (&buf)[RING], LoadF&& load) {
 #pragma unroll
     for (int b = 0; b < RING - 1; b++) load(min(it + b * W, n - 1), buf[b]);
+}
+template <int RING, typename Buf, typename LoadF, typename ComputeF>
+MOE_DEV void ring_run(int it, int W, int n, Buf (&buf)[RING], LoadF&& load, ComputeF&& compute) {
     bool more = true;
     while (more) {
 #pragma unroll
@@ -143,6 +160,11 @@ MOE_DEV void ring_walk(int it, int W, int n, Buf (&buf)[RING], LoadF&& load, Com
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the repeated tail loads land before the wave ends
+}
+template <int RING, typename Buf, typename LoadF, typename ComputeF>
+MOE_DEV void ring_walk(int it, int W, int n, Buf (&buf)[RING], LoadF&& load, ComputeF&& compute) {
+    ring_start<RING>(it, W, n, buf, load);
+    ring_run<RING>(it, W, n, buf, load, compute);
 }
 
 }  // namespace
@@ -163,17 +185,21 @@ __global__ __launch_bounds__(256) void k_gateup_stream(const uint16_t* __restric
     int* prow = reinterpret_cast<int*>(list + T * K);                          // [T*K] token of grouped row
     __shared__ int scan[4];
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
-    // the token rows go to LDS, then the touched list is built from the offsets
-    stage_lds(x, T * H * 2 / 1024, smem, wave, l);
-    for (int i = tid; i < T * K; i += 256) prow[i] = perm[i] / K;
+    // the grouped rows' tokens and the touched list (from the offsets) come
+    // first; then the first items' weight loads and all of the token rows'
+    // loads go out together, so the block waits for memory twice before it
+    // multiplies
+    const int pv = tid < T * K ? perm[tid] : 0;
     const int nlist = block_touched_list(offsets, E, list, scan);
+    if (tid < T * K) prow[tid] = pv / K;
+    for (int i = tid + 256; i < T * K; i += 256) prow[i] = perm[i] / K;
     __syncthreads();
 
     const int tpe = F / FR;                     // items per expert
     const int n_items = nlist * tpe;
     const int W = gridDim.x * 4;
-    int it = blockIdx.x * 4 + wave;
-    if (it >= n_items) return;
+    const int it = blockIdx.x * 4 + wave;
+    const bool active = it < n_items;
 
     uint4 wbuf[RING][2 * FR][CH];
     auto load = [&](int item, uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
@@ -190,32 +216,58 @@ __global__ __launch_bounds__(256) void k_gateup_stream(const uint16_t* __restric
     };
     auto compute = [&](int item, const uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
-        const int off = ent.y, n = ent.z, f0 = (item % tpe) * FR;
-        constexpr int V = 2 * FR * NT;
-        float acc[V];
+        const int off = ent.y, n = __builtin_amdgcn_readfirstlane(ent.z), f0 = (item % tpe) * FR;
+        auto rows = [&](auto ntn) __attribute__((always_inline)) {
+            constexpr int NTN = decltype(ntn)::value;
+            constexpr int V = 2 * FR * NTN;
+            float acc[V];
 #pragma unroll
-        for (int i = 0; i < V; i++) acc[i] = 0.f;
+            for (int i = 0; i < V; i++) acc[i] = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            if (t < n) {
-                const uint16_t* xr = xs + prow[off + t] * H + l * 8;
+            for (int t = 0; t < NTN; t++) {
+                if (t < n) {
+                    const uint16_t* xr = xs + prow[off + t] * H + l * 8;
 #pragma unroll
-                for (int c = 0; c < CH; c++) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(xr + c * 512);
+                    for (int c = 0; c < CH; c++) {
+                        const uint4 a = *reinterpret_cast<const uint4*>(xr + c * 512);
 #pragma unroll
-                    for (int r = 0; r < 2 * FR; r++) acc[r * NT + t] = dot8bf(w[r][c], a, acc[r * NT + t]);
+                        for (int r = 0; r < 2 * FR; r++) acc[r * NTN + t] = dot8bf(w[r][c], a, acc[r * NTN + t]);
+                    }
                 }
             }
-        }
-        // lane l owns entry j = l >> shift: row r = j / NT (< FR gate, else up), token t = j % NT
-        const float v = wave_tr_reduce<V>(acc);
-        constexpr int shift = tr_shift<V>();
-        const float up = __shfl_down(v, (FR * NT) << shift, WAVE);
-        const int j = l >> shift, r = j / NT, t = j % NT;
-        if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
-            abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+            // lane l owns entry j = l >> shift: row r = j / NTN (< FR gate, else up), token t = j % NTN
+            const float v = wave_tr_reduce<V>(acc);
+            constexpr int shift = tr_shift<V>();
+            const float up = __shfl_down(v, (FR * NTN) << shift, WAVE);
+            const int j = l >> shift, r = j / NTN, t = j % NTN;
+            if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
+                abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+        };
+        by_rows<NT>(n, rows);
     };
-    ring_walk<RING>(it, W, n_items, wbuf, load, compute);
+    // (for H > 2048 the first item's buffers are too large to hold across
+    // the staging: the loads go out after it)
+    constexpr bool early = CH <= 4;
+    if (early && active) ring_start<RING>(it, W, n_items, wbuf, load);
+    {
+        constexpr int MAXC = NT * H * 2 / 16 / 256;   // 16-byte chunks per thread for T = NT
+        constexpr int BATCH = MAXC < 8 ? MAXC : 8;
+        const int n16 = T * H * 2 / 16;
+        const uint4* g = reinterpret_cast<const uint4*>(x);
+#pragma unroll
+        for (int c0 = 0; c0 < MAXC; c0 += BATCH) {
+            uint4 r[BATCH];
+#pragma unroll
+            for (int c = 0; c < BATCH; c++) r[c] = g[min(tid + (c0 + c) * 256, n16 - 1)];
+#pragma unroll
+            for (int c = 0; c < BATCH; c++)   // past the end: the last chunk again, same value
+                reinterpret_cast<uint4*>(xs)[min(tid + (c0 + c) * 256, n16 - 1)] = r[c];
+        }
+    }
+    if (!early && active) ring_start<RING>(it, W, n_items, wbuf, load);
+    __syncthreads();
+    if (!active) return;
+    ring_run<RING>(it, W, n_items, wbuf, load, compute);
 }
 
 // down.  Item = (touched expert j, hidden tile): DR rows of Wd over the whole
@@ -262,27 +314,31 @@ __global__ __launch_bounds__(256) void k_down_stream(const uint16_t* __restrict_
     auto compute = [&](int item, const Buf& b) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
         const int off = ent.y, n = __builtin_amdgcn_readfirstlane(ent.z), h0 = (item % tpe) * DR;
-        constexpr int V = DR * NT;
-        float acc[V];
+        auto rows = [&](auto ntn) __attribute__((always_inline)) {
+            constexpr int NTN = decltype(ntn)::value;
+            constexpr int V = DR * NTN;
+            float acc[V];
 #pragma unroll
-        for (int i = 0; i < V; i++) acc[i] = 0.f;
+            for (int i = 0; i < V; i++) acc[i] = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            if (t < n) {
+            for (int t = 0; t < NTN; t++) {
+                if (t < n) {
 #pragma unroll
-                for (int c = 0; c < FCH; c++)
+                    for (int c = 0; c < FCH; c++)
 #pragma unroll
-                    for (int r = 0; r < DR; r++) acc[r * NT + t] = dot8bf(b.w[r][c], b.a[t][c], acc[r * NT + t]);
+                        for (int r = 0; r < DR; r++) acc[r * NTN + t] = dot8bf(b.w[r][c], b.a[t][c], acc[r * NTN + t]);
+                }
             }
-        }
-        const float v = wave_tr_reduce<V>(acc);
-        constexpr int shift = tr_shift<V>();
-        const int j = l >> shift, r = j / NT, t = j % NT;
-        if ((l & ((1 << shift) - 1)) == 0 && t < n) {
-            const long o = (long)(off + t) * H + h0 + r;
-            if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
-            else ((float*)y)[o] = v;
-        }
+            const float v = wave_tr_reduce<V>(acc);
+            constexpr int shift = tr_shift<V>();
+            const int j = l >> shift, r = j / NTN, t = j % NTN;
+            if ((l & ((1 << shift) - 1)) == 0 && t < n) {
+                const long o = (long)(off + t) * H + h0 + r;
+                if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
+                else ((float*)y)[o] = v;
+            }
+        };
+        by_rows<NT>(n, rows);
     };
     ring_walk<RING>(it, W, n_items, wbuf, load, compute);
 }
@@ -437,33 +493,38 @@ __global__ __launch_bounds__(256, (QB == 4 ? 1 : 2)) void k_gateup_stream_q4(con
     };
     auto compute = [&](int item, const Buf& b) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
-        const int off = ent.y, n = ent.z, f0 = (item % tpe) * FR;
-        constexpr int V = 2 * FR * NT;
-        float acc[V];
+        const int off = ent.y, n = __builtin_amdgcn_readfirstlane(ent.z), f0 = (item % tpe) * FR;
+        auto rows = [&](auto ntn) __attribute__((always_inline)) {
+            constexpr int NTN = decltype(ntn)::value;
+            constexpr int V = 2 * FR * NTN;
+            float acc[V];
 #pragma unroll
-        for (int i = 0; i < V; i++) acc[i] = 0.f;
+            for (int i = 0; i < V; i++) acc[i] = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            if (t < n) {
-                const int tok = prow[off + t];
+            for (int t = 0; t < NTN; t++) {
+                if (t < n) {
+                    const int tok = prow[off + t];
 #pragma unroll
-                for (int c = 0; c < CH; c++) {
-                    const uint16_t* xl = xs + tok * H + c * 2048 + l * 32;
-                    const float S = xsum[tok * (H / 32) + c * 64 + l];
+                    for (int c = 0; c < CH; c++) {
+                        const uint16_t* xl = xs + tok * H + c * 2048 + l * 32;
+                        const float S = xsum[tok * (H / 32) + c * 64 + l];
 #pragma unroll
-                    for (int r = 0; r < 2 * FR; r++) {
-                        const float D = dot_block<QB>(b.q[r][c], xl);
-                        acc[r * NT + t] = fmaf(fp16_to_f32(b.d[r][c]), fmaf(-zero_level<QB>(), S, D), acc[r * NT + t]);
+                        for (int r = 0; r < 2 * FR; r++) {
+                            const float D = dot_block<QB>(b.q[r][c], xl);
+                            acc[r * NTN + t] =
+                                fmaf(fp16_to_f32(b.d[r][c]), fmaf(-zero_level<QB>(), S, D), acc[r * NTN + t]);
+                        }
                     }
                 }
             }
-        }
-        const float v = wave_tr_reduce<V>(acc);
-        constexpr int shift = tr_shift<V>();
-        const float up = __shfl_down(v, (FR * NT) << shift, WAVE);
-        const int j = l >> shift, r = j / NT, t = j % NT;
-        if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
-            abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+            const float v = wave_tr_reduce<V>(acc);
+            constexpr int shift = tr_shift<V>();
+            const float up = __shfl_down(v, (FR * NTN) << shift, WAVE);
+            const int j = l >> shift, r = j / NTN, t = j % NTN;
+            if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < n)
+                abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+        };
+        by_rows<NT>(n, rows);
     };
     ring_walk<RING>(it, W, n_items, wbuf, load, compute);
 }
@@ -509,32 +570,36 @@ __global__ __launch_bounds__(256) void k_down_stream_q4(const uint16_t* __restri
     };
     auto compute = [&](int item, const Buf& bf) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
-        const int off = ent.y, n = ent.z, h0 = (item % tpe) * (4 * I);
-        constexpr int V = I * NT;
-        static_assert(V <= 16, "one entry per lane after the 16-lane reduction");
-        float acc[V];
+        const int off = ent.y, n = __builtin_amdgcn_readfirstlane(ent.z), h0 = (item % tpe) * (4 * I);
+        auto rows = [&](auto ntn) __attribute__((always_inline)) {
+            constexpr int NTN = decltype(ntn)::value;
+            constexpr int V = I * NTN;
+            static_assert(V <= 16, "one entry per lane after the 16-lane reduction");
+            float acc[V];
 #pragma unroll
-        for (int i = 0; i < V; i++) acc[i] = 0.f;
+            for (int i = 0; i < V; i++) acc[i] = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            if (t < n) {
-                const uint16_t* al = as + (off + t) * F + b * 32;
-                const float S = asum[(off + t) * NB + b];
+            for (int t = 0; t < NTN; t++) {
+                if (t < n) {
+                    const uint16_t* al = as + (off + t) * F + b * 32;
+                    const float S = asum[(off + t) * NB + b];
 #pragma unroll
-                for (int i = 0; i < I; i++) {
-                    const float D = dot_block<QB>(bf.q[i], al);
-                    acc[i * NT + t] = fmaf(fp16_to_f32(bf.d[i]), fmaf(-zero_level<QB>(), S, D), acc[i * NT + t]);
+                    for (int i = 0; i < I; i++) {
+                        const float D = dot_block<QB>(bf.q[i], al);
+                        acc[i * NTN + t] = fmaf(fp16_to_f32(bf.d[i]), fmaf(-zero_level<QB>(), S, D), acc[i * NTN + t]);
+                    }
                 }
             }
-        }
-        const float v = group16_tr_reduce<V>(acc);
-        constexpr int shift = V == 16 ? 0 : V == 8 ? 1 : V == 4 ? 2 : V == 2 ? 3 : 4;
-        const int j = b >> shift, i = j / NT, t = j % NT;
-        if ((b & ((1 << shift) - 1)) == 0 && t < n) {
-            const long o = (long)(off + t) * H + h0 + 4 * i + g;
-            if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
-            else ((float*)y)[o] = v;
-        }
+            const float v = group16_tr_reduce<V>(acc);
+            constexpr int shift = V == 16 ? 0 : V == 8 ? 1 : V == 4 ? 2 : V == 2 ? 3 : 4;
+            const int j = b >> shift, i = j / NTN, t = j % NTN;
+            if ((b & ((1 << shift) - 1)) == 0 && t < n) {
+                const long o = (long)(off + t) * H + h0 + 4 * i + g;
+                if constexpr (YBF16) ((uint16_t*)y)[o] = f32_to_bf16_rne(v);
+                else ((float*)y)[o] = v;
+            }
+        };
+        by_rows<NT>(n, rows);
     };
     ring_walk<RING>(it, W, n_items, wbuf, load, compute);
 }
