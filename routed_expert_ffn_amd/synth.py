@@ -343,12 +343,18 @@ def make_device_weights(s: LayerShape, seed: int, cfg: int, layer: int, device, 
     return res
 
 
+def make_device_activations(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0, device="cuda"):
+    """The layer's input rows [T][H] as make_device_layer draws them (same bytes)."""
+    torch = _torch()
+    xdt = torch.float32 if s.act == "f32" else torch.bfloat16
+    return _dev_normal((s.T, s.H), 1.0, seed, cfg, layer, TID_X, device, xdt)
+
+
 def make_device_layer(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0, device="cuda",
                       x=None) -> DeviceLayer:
     torch = _torch()
     if x is None:
-        xdt = torch.float32 if s.act == "f32" else torch.bfloat16
-        x = _dev_normal((s.T, s.H), 1.0, seed, cfg, layer, TID_X, device, xdt)
+        x = make_device_activations(s, seed, cfg, layer, device)
     wr = _dev_normal((s.E, s.H), 0.02, seed, cfg, layer, TID_WR, device, torch.float32)
     bias = zipf_bias_torch(s.E, seed, cfg, layer, device) if s.zipf else None
     w = make_device_weights(s, seed, cfg, layer, device)
