@@ -154,6 +154,29 @@ moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                            void* workspace, size_t ws_bytes, moe_stream stream);
 
+/* ---------------------------------------------------------------- routing + grouping, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_route_group with the same arguments and results, minus the workspace.
+ * Its scratch is a fixed 32 MiB device array inside the library, one copy per
+ * GPU, made when the library is loaded on that GPU and held until the process
+ * ends; its address is looked up once per device, on the first call made with
+ * that device current (the stream must belong to the current device).  This
+ * call allocates nothing and calls no allocating routine.
+ * Returns MOE_ERR_WORKSPACE, with nothing launched, when
+ * moe_route_group_workspace_size(T, H, E, K, x_dtype) exceeds 32 MiB (e.g.
+ * E = 512, H = 2048, K = 10: up to 13,107 tokens); MOE_ERR_HIP if the device
+ * array cannot be found.  Every call on one GPU uses that GPU's one array, so
+ * calls that overlap in time on one GPU (different streams, or host threads
+ * without ordering) race and give undefined results; calls on one stream are
+ * ordered and safe.  The array keeps the last call's contents; everything a
+ * call needs cleared is cleared by its own kernels. */
+moe_status moe_route_group_noalloc(const void* x, int32_t x_dtype, const float* w_router, const float* bias,
+                                   int32_t T, int32_t H, int32_t E, int32_t K,
+                                   int32_t* topk_idx, float* topk_w,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                   moe_stream stream);
+
 /* ---------------------------------------------------------------- experts
  * Grouped SwiGLU expert FFN (page 1 §3: gate, up and down per expert).  For
  * every permuted row p in expert e's segment [offsets[e], offsets[e+1]), with

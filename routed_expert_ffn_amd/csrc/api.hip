@@ -5,6 +5,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int MAX_E = 4096;
@@ -140,10 +142,15 @@ size_t moe_route_group_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K
     return round256(moe_route_workspace_size(T, H, E, K, x_dtype)) + moe_permute_workspace_size(T, K, E);
 }
 
-moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T,
-                           int32_t H, int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, int32_t* counts,
-                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes,
-                           moe_stream stream) {
+}  // extern "C"
+
+namespace {
+// moe_route_group's body on a given workspace (the caller's, or the per-GPU
+// scratch of moe_route_group_noalloc).
+moe_status route_group_on(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T,
+                          int32_t H, int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes,
+                          moe_stream stream) {
     const moe_status chk = route_check(x, x_dtype, w_router, T, H, E, K, topk_idx, topk_w);
     if (chk != MOE_OK) return chk;
     if (!counts || !offsets || (T > 0 && (!perm || !inv_perm))) return MOE_ERR_INVALID_ARG;
@@ -161,6 +168,58 @@ moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router
     if (r != MOE_OK) return r;
     return moe_permute(topk_idx, T, K, E, counts, offsets, perm, inv_perm, (char*)workspace + rws, ws_bytes - rws,
                        stream);
+}
+
+}  // namespace
+
+// The scratch of moe_route_group_noalloc: a fixed device array, one copy per
+// GPU (made when the library's code object is loaded on that GPU, held until
+// the process ends).  Host code must not use the array's name as an address:
+// its device address is looked up once per device and kept in scratch_ptr.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::once_flag scratch_once[NOALLOC_MAX_DEVICES];
+void* scratch_ptr[NOALLOC_MAX_DEVICES];
+hipError_t scratch_err[NOALLOC_MAX_DEVICES];
+
+// The current device's copy of `scratch` (its address looked up on the first
+// call made with that device current), or nullptr.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+    std::call_once(scratch_once[dev], [dev] {
+        void* p = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    return scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router, const float* bias, int32_t T,
+                           int32_t H, int32_t E, int32_t K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes,
+                           moe_stream stream) {
+    return route_group_on(x, x_dtype, w_router, bias, T, H, E, K, topk_idx, topk_w, counts, offsets, perm, inv_perm,
+                          workspace, ws_bytes, stream);
+}
+
+moe_status moe_route_group_noalloc(const void* x, int32_t x_dtype, const float* w_router, const float* bias,
+                                   int32_t T, int32_t H, int32_t E, int32_t K, int32_t* topk_idx, float* topk_w,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                   moe_stream stream) {
+    const moe_status chk = route_check(x, x_dtype, w_router, T, H, E, K, topk_idx, topk_w);
+    if (chk != MOE_OK) return chk;
+    if (moe_route_group_workspace_size(T, H, E, K, x_dtype) > NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = device_scratch();
+    if (!ws) return MOE_ERR_HIP;
+    return route_group_on(x, x_dtype, w_router, bias, T, H, E, K, topk_idx, topk_w, counts, offsets, perm, inv_perm,
+                          ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_t F, int32_t x_dtype,

@@ -19,7 +19,7 @@ _QUANT_BY_BITS = {4: INT4_B32, 3: INT3_B32, 2: INT2_B32}
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_ffn_workspace_size", "moe_ffn",
-           "moe_route_group_workspace_size", "moe_route_group", "moe_combine", "moe_combine_steer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
+           "moe_route_group_workspace_size", "moe_route_group", "moe_route_group_noalloc", "moe_combine", "moe_combine_steer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
            "moe_profile_hits", "moe_strp_size", "moe_strp_write", "moe_strp_read", "moe_profile_remap"]
 
 
@@ -75,6 +75,8 @@ def load():
     L.moe_route_group_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.moe_route_group.restype = ctypes.c_int
     L.moe_route_group.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_group_noalloc.restype = ctypes.c_int
+    L.moe_route_group_noalloc.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine_steer.restype = ctypes.c_int
     L.moe_combine_steer.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp]
     L.moe_expert_freq.restype = ctypes.c_int
@@ -235,6 +237,34 @@ def route_group(x, w_router, K: int, bias=None, workspace=None, stream=None, out
     _chk(load().moe_route_group(_ptr(x), _act_dtype(x), _ptr(w_router), _ptr(bias), T, H, E, K, _ptr(idx), _ptr(w),
                                 _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws), nb, _stream(stream)),
          "moe_route_group")
+    return idx, w, counts, offsets, perm, inv
+
+
+def route_group_noalloc(x, w_router, K: int, bias=None, stream=None, out=None):
+    """moe_route_group_noalloc: route_group on the library's own per-GPU
+    scratch (no workspace argument, nothing allocated by the library).
+    Returns (idx, w, counts, offsets, perm, inv); out: optional 6-tuple to fill."""
+    _need(x, "x")
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(w_router, "w_router", torch.float32, (E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    dev = x.device
+    if out is not None:
+        idx, w, counts, offsets, perm, inv = out
+        for n, t, dt, shp in (("topk_idx", idx, torch.int32, (T, K)), ("topk_w", w, torch.float32, (T, K)),
+                              ("counts", counts, torch.int32, (E,)), ("offsets", offsets, torch.int32, (E + 1,)),
+                              ("perm", perm, torch.int32, (T * K,)), ("inv_perm", inv, torch.int32, (T * K,))):
+            _need(t, n, dt, shp)
+    else:
+        i32 = dict(dtype=torch.int32, device=dev)
+        idx, w = torch.empty((T, K), **i32), torch.empty((T, K), dtype=torch.float32, device=dev)
+        counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+        perm, inv = torch.empty(T * K, **i32), torch.empty(T * K, **i32)
+    _chk(load().moe_route_group_noalloc(_ptr(x), _act_dtype(x), _ptr(w_router), _ptr(bias), T, H, E, K, _ptr(idx),
+                                        _ptr(w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
+                                        _stream(stream)), "moe_route_group_noalloc")
     return idx, w, counts, offsets, perm, inv
 
 

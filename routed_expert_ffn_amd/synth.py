@@ -350,13 +350,19 @@ def make_device_activations(s: LayerShape, seed: int = 0, cfg: int = 0, layer: i
     return _dev_normal((s.T, s.H), 1.0, seed, cfg, layer, TID_X, device, xdt)
 
 
-def make_device_layer(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0, device="cuda",
-                      x=None) -> DeviceLayer:
+def make_device_router(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0, device="cuda"):
+    """(router weights [E][H] fp32, Zipf offset [E] fp32 or None) as make_device_layer draws them."""
     torch = _torch()
-    if x is None:
-        x = make_device_activations(s, seed, cfg, layer, device)
     wr = _dev_normal((s.E, s.H), 0.02, seed, cfg, layer, TID_WR, device, torch.float32)
     bias = zipf_bias_torch(s.E, seed, cfg, layer, device) if s.zipf else None
+    return wr, bias
+
+
+def make_device_layer(s: LayerShape, seed: int = 0, cfg: int = 0, layer: int = 0, device="cuda",
+                      x=None) -> DeviceLayer:
+    if x is None:
+        x = make_device_activations(s, seed, cfg, layer, device)
+    wr, bias = make_device_router(s, seed, cfg, layer, device)
     w = make_device_weights(s, seed, cfg, layer, device)
     return DeviceLayer(s, x, wr, bias, w[TID_WG][0], w[TID_WU][0], w[TID_WD][0],
                        w[TID_WG][1], w[TID_WU][1], w[TID_WD][1])
