@@ -112,13 +112,17 @@ const char* moe_status_string(moe_status s);
  * products x*w taken in wave-64 order (64 strided partial sums, then a pairwise
  * tree 32,16,...,1); the selection is exact with respect to these values.  A
  * faster fp32 estimate is used where every gap among the leading K+1 logits
- * clears a safety margin of 2^-12; other tokens are re-decided on the exact
- * values.  The estimate (bf16 activations, T >= 64, logits_out NULL) is exact
- * in every product and rounds only in its fp32 accumulation, so the selection
- * stays exact while that error stays below half the margin: measured below
- * 1e-6 for activations ~N(0,1) and router weights ~N(0,0.02) at H = 2048, and
- * growing in proportion to |x| |w|.  Passing logits_out selects the exact
- * logits for every token.
+ * clears a safety margin; other tokens are re-decided on the exact values.
+ * The estimate (bf16 activations, T >= 64, logits_out NULL) is exact in every
+ * product and rounds only in its fp32 accumulation, so the selection stays
+ * exact while that error stays below half the margin.  The error grows in
+ * proportion to |x_t| and the router rows' norms, and so does the margin:
+ * token t's is max(2^-12, 2^-24 sqrt(H) |x_t|_2 max_e |w_e|_2).  For
+ * activations ~N(0,1) and router weights ~N(0,0.02) at H = 2048 the margin is
+ * 2^-12 and the measured error below 1e-6, over 100 times smaller than half
+ * the margin, and scaling x or w_router keeps that ratio.  This is a measured
+ * margin, not a proven bound: passing logits_out selects the exact logits for
+ * every token.
  * Unsupported: K > 32, E > 4096, H % 8 != 0.  NaN logits give unspecified
  * selections. */
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t x_dtype);
@@ -128,7 +132,10 @@ moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, cons
                      void* workspace, size_t ws_bytes, moe_stream stream);
 
 /* ---------------------------------------------------------------- grouping
- * Token->expert grouping: a stable counting sort of the flat slots
+ * Token->expert grouping (the kwkr.cn Coder write-up, "为什么 Coder 快" part 2:
+ * work is done per expert, for the experts a batch of tokens actually hits;
+ * grouping the routed slots by expert lets each touched expert's weights be
+ * read once for all of its rows): a stable counting sort of the flat slots
  * s = t*K + k by expert id.
  *   counts   [E]     int32 out: slots per expert.
  *   offsets  [E+1]   int32 out: exclusive scan of counts (offsets[E] = T*K).
@@ -165,7 +172,7 @@ moe_status moe_route_group(const void* x, int32_t x_dtype, const float* w_router
  * call allocates nothing and calls no allocating routine.
  * Returns MOE_ERR_WORKSPACE, with nothing launched, when
  * moe_route_group_workspace_size(T, H, E, K, x_dtype) exceeds 32 MiB (e.g.
- * E = 512, H = 2048, K = 10: up to 13,107 tokens); MOE_ERR_HIP if the device
+ * E = 512, H = 2048, K = 10: up to 13,106 tokens); MOE_ERR_HIP if the device
  * array cannot be found.  Every call on one GPU uses that GPU's one array, so
  * calls that overlap in time on one GPU (different streams, or host threads
  * without ordering) race and give undefined results; calls on one stream are
@@ -200,6 +207,9 @@ moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w,
                    void* workspace, size_t ws_bytes, moe_stream stream);
 
 /* ---------------------------------------------------------------- combine
+ * The layer's output (page 1 §1: 10 experts work on every token, so a token's
+ * output is its selected experts' outputs weighted by the routing weights;
+ * the stacked layers add it to the residual stream):
  *   out[t] = cast( sum_k topk_w[t][k] * y_perm[inv_perm[t*K+k]] + residual[t] )
  * accumulated in fp32 in k order (a gather: deterministic), one final
  * rounding to out_dtype (bf16: nearest-even).  residual [T][H] in out_dtype, or

@@ -48,7 +48,7 @@ const char* moe_status_string(moe_status s) {
 // bf16 planes for the estimate.
 namespace {
 struct RouteWs {
-    size_t flags, count, list, planes, total;
+    size_t flags, count, list, planes, wnorm, total;
 };
 RouteWs route_ws_layout(int T, int H, int E, int x_dtype) {
     RouteWs w;
@@ -56,9 +56,12 @@ RouteWs route_ws_layout(int T, int H, int E, int x_dtype) {
     w.count = w.flags + round256((size_t)T * sizeof(int32_t));
     w.list = w.count + 256;
     w.planes = w.list + round256((size_t)T * 8);
+    w.wnorm = w.planes;
     w.total = w.planes;
-    if (x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && logits_fast_eligible(T, H, E))
-        w.total += round256(logits_fast_planes_bytes(H, E));
+    if (x_dtype == MOE_BF16 && T >= FAST_ROUTE_MIN_T && logits_fast_eligible(T, H, E)) {
+        w.wnorm = w.planes + round256(logits_fast_planes_bytes(H, E));
+        w.total = w.wnorm + round256((size_t)E * sizeof(float));
+    }
     return w;
 }
 }  // namespace
@@ -103,16 +106,17 @@ moe_status moe_route(const void* x, int32_t x_dtype, const float* w_router, cons
     const int xb = x_dtype == MOE_BF16;
     hipError_t err;
     if (fast_route_eligible(T, H, E, x_dtype, x, w_router, logits_out)) {
-        err = launch_logits_fast((const uint16_t*)x, w_router, bias, T, H, E, lg, (uint16_t*)(wb + L.planes),
+        float* wnorm2 = (float*)(wb + L.wnorm);
+        err = launch_logits_fast((const uint16_t*)x, w_router, bias, T, H, E, lg, (uint16_t*)(wb + L.planes), wnorm2,
                                  rc_count, st);
         if (err != hipSuccess) return MOE_ERR_HIP;
-        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, topk_idx, topk_w, flags,
-                                  rc_list, rc_count, st);
+        err = launch_route_select(lg, T, E, K, ROUTE_TAU, 0, x, xb, w_router, bias, H, wnorm2, topk_idx, topk_w,
+                                  flags, rc_list, rc_count, st);
     } else {
         float* dst = logits_out ? logits_out : lg;
         err = launch_logits_exact(x, xb, w_router, bias, T, H, E, dst, st);
         if (err != hipSuccess) return MOE_ERR_HIP;
-        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, topk_idx, topk_w, flags, rc_list,
+        err = launch_route_select(dst, T, E, K, 0.f, 1, x, xb, w_router, bias, H, nullptr, topk_idx, topk_w, flags, rc_list,
                                   rc_count, st);
     }
     return hip_status(err);

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "device.h"
 #include "launch.h"
 
 namespace {
@@ -605,17 +606,13 @@ static hipError_t launch_one(int items, hipStream_t st, const uint16_t* src, con
                              const int32_t* perm, int K, int H, int F, void* out) {
     auto kern = k_gemm<BM, BN, PHASE, YBF16, WQ>;
     const int lds = Geo<BM, BN, WQ>::LDS;
-    static bool attr = false;     // raising the dynamic LDS limit is per function, once
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static LdsLimit lim;          // this instantiation's LDS limit, raised once per device
+    hipError_t e = lim.ensure((const void*)kern, lds);
+    if (e != hipSuccess) return e;
     // persistent: as many blocks as the CUs hold at once (one or two per CU,
     // by LDS), a multiple of the 8 XCDs
-    int dev = 0, ncu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int ncu = 0;
+    e = current_device_cus(&ncu);
     if (e != hipSuccess) return e;
     const int slots = ncu * Geo<BM, BN, WQ>::BLOCKS_PER_CU;
     const int cap = slots / 8 * 8 > 8 ? slots / 8 * 8 : 8;

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "device.h"
 #include "launch.h"
 
 namespace {
@@ -615,15 +616,9 @@ size_t gu_lds(int T, int K, int H) { return (size_t)T * H * 2 + (size_t)T * K * 
 size_t dn_lds(int T, int K, int F) { (void)T; (void)K; (void)F; return 0; }   // rows are loaded per item
 
 int stream_grid(hipError_t& err) {
-    int dev = 0, ncu = 0;
-    err = hipGetDevice(&dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int ncu = 0;
+    err = current_device_cus(&ncu);
     return 2 * (ncu > 0 ? ncu : 1);
-}
-
-template <typename KF>
-hipError_t set_lds(KF kern, size_t lds) {
-    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 template <int NT, int CH>
@@ -631,7 +626,8 @@ hipError_t gu_launch(int grid, hipStream_t st, const uint16_t* x, const void* wg
                      const int32_t* offsets, const int32_t* perm, int T, int K, int E, int F, uint16_t* abuf) {
     auto kern = k_gateup_stream<NT, CH, GU_FR, GU_RING>;
     const size_t lds = gu_lds(T, K, CH * 512);
-    hipError_t e = set_lds(kern, lds);
+    static LdsLimit lim;   // this launcher's kernel: raise its LDS limit once per device
+    hipError_t e = lim.ensure((const void*)kern, (int)STREAM_LDS_MAX);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, x, (const uint16_t*)wg, (const uint16_t*)wu, offsets,
                        perm, T, K, E, F, abuf);
@@ -643,7 +639,8 @@ hipError_t dn_launch(int grid, hipStream_t st, const uint16_t* abuf, const void*
                      int nrows, int T, int K, int E, int H, void* y) {
     auto kern = k_down_stream<NT, FCH, DN_DR, YB, DN_RING>;
     const size_t lds = dn_lds(T, K, FCH * 512);
-    hipError_t e = set_lds(kern, lds);
+    static LdsLimit lim;   // this launcher's kernel: raise its LDS limit once per device
+    hipError_t e = lim.ensure((const void*)kern, (int)STREAM_LDS_MAX);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, abuf, (const uint16_t*)wd, offsets, nrows, E, H, y);
     return hipSuccess;
@@ -683,7 +680,8 @@ hipError_t gu_launch_q4(int grid, hipStream_t st, const uint16_t* x, const void*
                         uint16_t* abuf) {
     auto kern = k_gateup_stream_q4<NT, CH, Q4_FR, Q_RING, QB>;
     const size_t lds = gu_lds_q4(T, K, CH * 2048);
-    hipError_t e = set_lds(kern, lds);
+    static LdsLimit lim;   // this launcher's kernel: raise its LDS limit once per device
+    hipError_t e = lim.ensure((const void*)kern, (int)STREAM_LDS_MAX);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, x, (const uint8_t*)wg, (const uint8_t*)wu,
                        (const uint16_t*)sg, (const uint16_t*)su, offsets, perm, T, K, E, F, abuf);
@@ -694,7 +692,8 @@ hipError_t dn_launch_q4(int grid, hipStream_t st, const uint16_t* abuf, const vo
                         const int32_t* offsets, int T, int K, int E, int H, void* y) {
     auto kern = k_down_stream_q4<NT, Q4_I, YB, Q_RING, QB>;
     const size_t lds = dn_lds_q4(T, K);
-    hipError_t e = set_lds(kern, lds);
+    static LdsLimit lim;   // this launcher's kernel: raise its LDS limit once per device
+    hipError_t e = lim.ensure((const void*)kern, (int)STREAM_LDS_MAX);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, abuf, (const uint8_t*)wd, (const uint16_t*)sd, offsets,
                        T * K, E, H, y);

@@ -10,14 +10,18 @@ hipError_t launch_logits_exact(const void* x, int x_bf16, const float* wr, const
 bool logits_fast_eligible(int T, int H, int E);
 size_t logits_fast_planes_bytes(int H, int E);
 // the estimate (three-plane bf16 split of the router, then the MFMA GEMM); the
-// split kernel also clears *rc_count, the recheck queue's counter
+// split kernel also stores each router row's squared norm in wnorm2 [E] and
+// clears *rc_count, the recheck queue's counter
 hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, uint16_t* planes, int32_t* rc_count, hipStream_t st);
-// selection; with estimates (exact == 0) tokens within tau are queued in
-// rc_list / rc_count and re-decided on exact logits by a second kernel
+                              float* logits, uint16_t* planes, float* wnorm2, int32_t* rc_count, hipStream_t st);
+// selection; with estimates (exact == 0, bf16 x, wnorm2 from the split) tokens
+// whose leading gaps fall within their margin (tau, scaled up with |x_t| and
+// the largest router row norm) are queued in rc_list / rc_count and re-decided
+// on exact logits by a second kernel
 hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
-                               int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                               int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st);
+                               int x_bf16, const float* wr, const float* bias, int H, const float* wnorm2,
+                               int32_t* idx, float* w, int32_t* flags, int2* rc_list, int32_t* rc_count,
+                               hipStream_t st);
 // A few tokens on exact logits: selection and grouping in one launch (route.hip)
 bool route_group_fused_eligible(int T, int K, int E);
 hipError_t launch_route_select_group(const float* logits, int T, int E, int K, int32_t* idx, float* w,

@@ -25,6 +25,7 @@
 // them or let an outside expert in); any other token recomputes the exact
 // logits of every expert within tau of its K-th value and selects among those.
 #include "common.h"
+#include "device.h"
 #include "group.h"
 #include "launch.h"
 
@@ -136,35 +137,49 @@ __global__ __launch_bounds__(256) void k_logits_exact(const XT* __restrict__ x, 
 // The router weight split once per call: w = hi + mid + lo exactly, each a
 // bf16 (8 significant bits each cover fp32's 24), stored as three planes
 // [3][E][H] so the estimate is a plain bf16 GEMM of x against all three.
-// Thread 0 also clears the recheck queue's counter for the selection that follows.
-__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ wr, long n4,
+// One block per router row; the block also stores the row's squared norm
+// (summed in a fixed order) for the selection's error margin, and thread 0 of
+// block 0 clears the recheck queue's counter for the selection that follows.
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ wr, int H,
                                                       uint16_t* __restrict__ planes, long plane_elems,
-                                                      int32_t* __restrict__ rc_count) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i == 0) rc_count[0] = 0;
-    if (i >= n4) return;
-    const float4 wv = reinterpret_cast<const float4*>(wr)[i];
-    const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
-    uint32_t hi[2], mi[2], lo[2];
+                                                      float* __restrict__ wnorm2, int32_t* __restrict__ rc_count) {
+    __shared__ float part[4];
+    const int e = blockIdx.x;
+    if (e == 0 && threadIdx.x == 0) rc_count[0] = 0;
+    const int h4 = H / 4;
+    float sq = 0.f;
+#pragma unroll 4
+    for (int j = threadIdx.x; j < h4; j += 256) {
+        const long i = (long)e * h4 + j;
+        const float4 wv = reinterpret_cast<const float4*>(wr)[i];
+        const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t hi[2], mi[2], lo[2];
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-        uint16_t h16[2], m16[2], l16[2];
+        for (int q = 0; q < 2; q++) {
+            uint16_t h16[2], m16[2], l16[2];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const float w = w4[q * 2 + u];
-            h16[u] = f32_to_bf16_rne(w);
-            const float r1 = w - bf16_to_f32(h16[u]);
-            m16[u] = f32_to_bf16_rne(r1);
-            const float r2 = r1 - bf16_to_f32(m16[u]);
-            l16[u] = f32_to_bf16_rne(r2);
+            for (int u = 0; u < 2; u++) {
+                const float w = w4[q * 2 + u];
+                sq = fmaf(w, w, sq);
+                h16[u] = f32_to_bf16_rne(w);
+                const float r1 = w - bf16_to_f32(h16[u]);
+                m16[u] = f32_to_bf16_rne(r1);
+                const float r2 = r1 - bf16_to_f32(m16[u]);
+                l16[u] = f32_to_bf16_rne(r2);
+            }
+            hi[q] = h16[0] | ((uint32_t)h16[1] << 16);
+            mi[q] = m16[0] | ((uint32_t)m16[1] << 16);
+            lo[q] = l16[0] | ((uint32_t)l16[1] << 16);
         }
-        hi[q] = h16[0] | ((uint32_t)h16[1] << 16);
-        mi[q] = m16[0] | ((uint32_t)m16[1] << 16);
-        lo[q] = l16[0] | ((uint32_t)l16[1] << 16);
+        reinterpret_cast<uint2*>(planes)[i] = make_uint2(hi[0], hi[1]);
+        reinterpret_cast<uint2*>(planes + plane_elems)[i] = make_uint2(mi[0], mi[1]);
+        reinterpret_cast<uint2*>(planes + 2 * plane_elems)[i] = make_uint2(lo[0], lo[1]);
     }
-    reinterpret_cast<uint2*>(planes)[i] = make_uint2(hi[0], hi[1]);
-    reinterpret_cast<uint2*>(planes + plane_elems)[i] = make_uint2(mi[0], mi[1]);
-    reinterpret_cast<uint2*>(planes + 2 * plane_elems)[i] = make_uint2(lo[0], lo[1]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sq += __shfl_xor(sq, d, WAVE);
+    if (lane_id() == 0) part[threadIdx.x / WAVE] = sq;
+    __syncthreads();
+    if (threadIdx.x == 0) wnorm2[e] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // Estimate GEMM: block tile 128 tokens x 128 experts, K step 64, two LDS stages
@@ -380,9 +395,16 @@ MOE_DEV void write_selection(float sel_v, int sel_i, int K, long t, int32_t* __r
 // a token whose K+1 leading values are all separated by at least tau is final
 // too; any other token is queued, with its cut (K-th estimate - tau), for
 // k_route_recheck and written there.
+//
+// The margin of a token is tau_t = max(tau, tau_scale * |x_t| * max_e |w_e|)
+// (Euclidean norms; tau_scale = 2^-24 sqrt(H)): the estimate's accumulation
+// error grows in proportion to the magnitudes of x and of the router rows,
+// so the margin keeps its headroom over that error when either is scaled.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ logits, int T, int E, int K,
-                                                      float tau, int exact, int32_t* __restrict__ idx_out,
+                                                      float tau, int exact, const uint16_t* __restrict__ xb, int H,
+                                                      const float* __restrict__ wnorm2, float tau_scale,
+                                                      int32_t* __restrict__ idx_out,
                                                       float* __restrict__ w_out, int32_t* __restrict__ rechecked,
                                                       int2* __restrict__ rc_list, int32_t* __restrict__ rc_count) {
     const int wave = threadIdx.x / WAVE;
@@ -395,6 +417,27 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     for (int j = 0; j < VPL; j++) {
         const int e = l + j * WAVE;
         kv[j] = e < E ? f32_order_key(row[e]) : 0u;
+    }
+    if (!exact) {
+        float xs = 0.f, wm = 0.f;
+        const uint4* xr = reinterpret_cast<const uint4*>(xb + (long)t * H);
+        for (int c = l; c < H / 8; c += WAVE) {
+            const uint4 v = xr[c];
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float a = bf16lo_to_f32(q[u]), b = bf16hi_to_f32(q[u]);
+                xs = fmaf(a, a, xs);
+                xs = fmaf(b, b, xs);
+            }
+        }
+        for (int e = l; e < E; e += WAVE) wm = fmaxf(wm, wnorm2[e]);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            xs += __shfl_xor(xs, d, WAVE);
+            wm = fmaxf(wm, __shfl_xor(wm, d, WAVE));
+        }
+        tau = fmaxf(tau, tau_scale * sqrtf(xs * wm));
     }
     const int rounds = (exact || K == E) ? K : K + 1;
     uint32_t key;
@@ -626,17 +669,11 @@ bool logits_fast_eligible(int T, int H, int E) {
 size_t logits_fast_planes_bytes(int H, int E) { return (size_t)3 * E * H * 2; }
 
 hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, uint16_t* planes, int32_t* rc_count, hipStream_t st) {
-    const long n4 = (long)E * H / 4;
-    hipLaunchKernelGGL(k_router_split, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, wr, n4, planes,
-                       (long)E * H, rc_count);
-    static bool attr = false;     // raising the dynamic LDS limit is per function, once
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_logits_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           2 * LM_STAGE);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+                              float* logits, uint16_t* planes, float* wnorm2, int32_t* rc_count, hipStream_t st) {
+    hipLaunchKernelGGL(k_router_split, dim3(E), dim3(256), 0, st, wr, H, planes, (long)E * H, wnorm2, rc_count);
+    static LdsLimit lim;          // the estimate GEMM's LDS limit, raised once per device
+    hipError_t e = lim.ensure((const void*)k_logits_mfma, 2 * LM_STAGE);
+    if (e != hipSuccess) return e;
     const int items = ((T + LM_BM - 1) / LM_BM) * ((E + LM_BN - 1) / LM_BN);
     hipLaunchKernelGGL(k_logits_mfma, dim3((items + 7) / 8 * 8), dim3(256), 2 * LM_STAGE, st, x, planes, bias, T, H, E,
                        logits);
@@ -645,10 +682,12 @@ hipError_t launch_logits_fast(const uint16_t* x, const float* wr, const float* b
 
 template <int VPL>
 static hipError_t sel_dispatch(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
-                               int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                               int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st) {
-    hipLaunchKernelGGL((k_route_select<VPL>), dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K, tau, exact, idx, w,
-                       flags, rc_list, rc_count);
+                               int x_bf16, const float* wr, const float* bias, int H, const float* wnorm2,
+                               int32_t* idx, float* w, int32_t* flags, int2* rc_list, int32_t* rc_count,
+                               hipStream_t st) {
+    const float tau_scale = ldexpf(sqrtf((float)H), -24);
+    hipLaunchKernelGGL((k_route_select<VPL>), dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K, tau, exact,
+                       (const uint16_t*)x, H, wnorm2, tau_scale, idx, w, flags, rc_list, rc_count);
     if (exact) return hipGetLastError();
     const int grid = T < 256 ? T : 256;
     if (x_bf16)
@@ -661,10 +700,12 @@ static hipError_t sel_dispatch(const float* logits, int T, int E, int K, float t
 }
 
 hipError_t launch_route_select(const float* logits, int T, int E, int K, float tau, int exact, const void* x,
-                               int x_bf16, const float* wr, const float* bias, int H, int32_t* idx, float* w,
-                               int32_t* flags, int2* rc_list, int32_t* rc_count, hipStream_t st) {
+                               int x_bf16, const float* wr, const float* bias, int H, const float* wnorm2,
+                               int32_t* idx, float* w, int32_t* flags, int2* rc_list, int32_t* rc_count,
+                               hipStream_t st) {
+    if (!exact && (!x_bf16 || !wnorm2 || H % 8 != 0)) return hipErrorInvalidValue;
     const int vpl = (E + WAVE - 1) / WAVE;
-#define MOE_SEL(V) return sel_dispatch<V>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, idx, w, flags, rc_list, rc_count, st)
+#define MOE_SEL(V) return sel_dispatch<V>(logits, T, E, K, tau, exact, x, x_bf16, wr, bias, H, wnorm2, idx, w, flags, rc_list, rc_count, st)
     if (vpl <= 1) MOE_SEL(1);
     if (vpl <= 2) MOE_SEL(2);
     if (vpl <= 4) MOE_SEL(4);

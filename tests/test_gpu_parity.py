@@ -217,6 +217,50 @@ def test_route_recheck_falls_back_to_all_experts():
     _route_case(x, wr, K, bias)
 
 
+def _rechecked_tokens(xd, wr, K):
+    """moe_route on the estimate path; returns (ids, weights, number of tokens re-decided on exact logits)."""
+    T, E = xd.shape[0], wr.shape[0]
+    ws = torch.empty(moe.route_workspace_size(T, xd.shape[1], E, K), dtype=torch.uint8, device="cuda")
+    idx, w = moe.route(xd, wr, K, workspace=ws)
+    torch.cuda.synchronize()
+    off = (T * E * 4 + 255) // 256 * 256              # the per-token recheck flags follow the [T][E] estimates
+    flags = ws[off:off + T * 4].view(torch.int32)
+    return idx, w, int(flags.sum().item())
+
+
+def test_route_margin_follows_input_magnitude():
+    """The estimate's margin grows with |x_t| and the router rows' norms (its
+    accumulation error does): with activations or router weights scaled by
+    powers of two (exact in bf16 / fp32) the selection stays bit-exact, and at
+    large scales a comparable share of tokens is still re-decided on exact
+    logits (a fixed margin would let them through on estimates whose error has
+    grown with the scale)."""
+    rng = np.random.default_rng(31)
+    T, H, E, K = 1024, 2048, 512, 10
+    x32 = rng.standard_normal((T, H)).astype(np.float32)
+    w32 = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    base = None
+    for xs, ws in ((1.0, 1.0), (1024.0, 1.0), (1.0, 256.0), (2.0 ** -8, 1.0)):
+        x = synth.f32_to_bf16_bits(x32 * np.float32(xs))
+        wr = (w32 * np.float32(ws)).astype(np.float32)
+        xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        idx, w, n_re = _rechecked_tokens(xd, torch.from_numpy(wr).cuda(), K)
+        ref_idx, ref_w, _ = oracle.route(x, wr, K)
+        assert np.array_equal(to_host(idx), ref_idx), f"ids differ with x*{xs}, w*{ws}"
+        # weights of tokens decided on estimates come from the estimates, whose
+        # error (and so the weights' relative error) grows with the scale; at
+        # large scales the smallest weights reach fp32's subnormal range, which
+        # the GPU's exp may flush to zero (hence the absolute floor)
+        tol = TOL_W * max(1.0, xs * ws)
+        g, r = to_host(w).astype(np.float64), ref_w.astype(np.float64)
+        assert np.all(np.abs(g - r) <= tol * np.abs(r) + 1e-30), f"weights off with x*{xs}, w*{ws}"
+        if base is None:
+            base = n_re
+            assert base > 0
+        elif xs * ws > 1:
+            assert n_re >= base // 4, f"x*{xs}, w*{ws}: {n_re} tokens re-decided (unscaled: {base})"
+
+
 def test_route_and_grouping_empty():
     wr = torch.zeros((8, 64), dtype=torch.float32, device="cuda")
     x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")

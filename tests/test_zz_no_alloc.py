@@ -52,8 +52,23 @@ def test_noalloc_matches_route_group_on_calls_in_a_row():
             assert weight_rel_err(to_host(got["w"]), ref_w) <= TOL_W
 
 
+SCRATCH_BYTES = 32 << 20
+
+
+def largest_fitting_T(E, H=2048, K=10):
+    lo, hi = 1, 1 << 20
+    while lo < hi:
+        m = (lo + hi + 1) // 2
+        if moe.route_group_workspace_size(m, H, E, K) <= SCRATCH_BYTES:
+            lo = m
+        else:
+            hi = m - 1
+    return lo
+
+
 def test_noalloc_rejects_sizes_beyond_its_scratch():
-    s, x, wr, bias = inputs(13108, 512, False, 3)
+    t_max = largest_fitting_T(512)
+    s, x, wr, bias = inputs(t_max + 1, 512, False, 3)
     idx = torch.full((s.T, s.K), -7, dtype=torch.int32, device="cuda")
     w = torch.full((s.T, s.K), -7.0, dtype=torch.float32, device="cuda")
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -65,7 +80,7 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     torch.cuda.synchronize()
     assert bool((idx == -7).all()) and bool((w == -7.0).all()) and all(bool((t == -7).all()) for t in rest)
     # the largest size that fits still runs, and matches
-    s, x, wr, bias = inputs(13107, 512, False, 3)
+    s, x, wr, bias = inputs(t_max, 512, False, 3)
     ref, got = both(s, x, wr, bias)
     for n in NAMES:
-        assert torch.equal(got[n], ref[n]), f"T=13107: {n} differs from moe_route_group"
+        assert torch.equal(got[n], ref[n]), f"T={t_max}: {n} differs from moe_route_group"
