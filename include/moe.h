@@ -195,8 +195,9 @@ moe_status moe_route_group_noalloc(const void* x, int32_t x_dtype, const float* 
  * Built combinations: (x F32, weights F32, y F32), (x BF16, weights BF16,
  * y BF16 or F32), (x BF16, weights INT4_B32, y BF16 or F32), and for the
  * verify and decode steps (x BF16, weights INT3_B32 or INT2_B32, y BF16 or
- * F32) with T <= 8, H = 2048, F = 512 (the lower-bit expert variant; other
- * shapes return MOE_ERR_UNSUPPORTED).
+ * F32) with T <= 8, T*K <= 59, H = 2048, F = 512 (the lower-bit expert
+ * variant; other shapes return MOE_ERR_UNSUPPORTED; moe_layer takes these
+ * weights up to T*K = 128).
  * Unsupported: H or F not a multiple of 64. */
 size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_t F, int32_t x_dtype,
                               int32_t w_dtype);
@@ -235,6 +236,31 @@ moe_status moe_combine_steer(const void* y_perm, int32_t y_dtype, const int32_t*
                              const float* topk_w, const void* residual, const float* steer_v,
                              int32_t T, int32_t K, int32_t H, void* out, int32_t out_dtype,
                              moe_stream stream);
+
+/* ---------------------------------------------------------------- one whole layer
+ * The MoE layer in one call (page 1 §1: every token routed to K experts whose
+ * outputs are combined with the routing weights; §3: gate, up and down per
+ * expert): moe_route_group, moe_ffn and moe_combine (moe_combine_steer when
+ * steer_v is given) with the same arguments and meanings, and
+ *     out[t] = cast( sum_k topk_w[t][k] * FFN_{topk_idx[t][k]}(x[t]) + residual[t] )
+ * in x's dtype.  The routing and grouping outputs are produced as those calls
+ * produce them.  residual [T][H] (x's dtype) or NULL; out [T][H] may alias x
+ * and residual (an in-place residual stream).  steer_v [H] fp32 or NULL.
+ * For a few tokens (T <= 8, T*K <= 128, H = 2048, F = 512, E <= 1024, bf16
+ * activations, bf16 or block-quantised weights, 16-byte aligned tensors) the
+ * layer runs as three launches: the exact logits; the selection and grouping
+ * (redone by every block of the gate/up launch) with the gate/up projections;
+ * the down projections with the combine, the expert outputs kept in fp32
+ * (no y_perm).  Other shapes run the three calls as they are (y_perm in x's
+ * dtype).  Errors as for those calls; workspace:
+ * moe_layer_workspace_size(T, H, E, K, F, x_dtype, w_dtype) bytes. */
+size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t F, int32_t x_dtype,
+                                int32_t w_dtype);
+moe_status moe_layer(const void* x, int32_t x_dtype, const float* w_router, const float* bias,
+                     const moe_expert_weights* w, int32_t T, int32_t H, int32_t E, int32_t K, int32_t F,
+                     const void* residual, const float* steer_v, void* out,
+                     int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                     int32_t* perm, int32_t* inv_perm, void* workspace, size_t ws_bytes, moe_stream stream);
 
 /* ---------------------------------------------------------------- pruning statistic
  * Per-(layer, expert) selection counts over given router logits (page 1 §3:

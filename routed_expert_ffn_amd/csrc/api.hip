@@ -232,9 +232,13 @@ size_t moe_ffn_workspace_size(int32_t T, int32_t K, int32_t E, int32_t H, int32_
     return ffn_workspace_bytes(T, K, E, H, F, x_dtype, w_dtype) + 256;
 }
 
-moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, const int32_t* offsets,
-                   const int32_t* perm, int32_t T, int32_t K, int32_t H, int32_t F, int32_t E, void* y_perm,
-                   int32_t y_dtype, void* workspace, size_t ws_bytes, moe_stream stream) {
+}  // extern "C"
+
+namespace {
+// moe_ffn's argument checks (everything but the workspace)
+moe_status ffn_check(const void* x, int32_t x_dtype, const moe_expert_weights* w, const int32_t* offsets,
+                     const int32_t* perm, int32_t T, int32_t K, int32_t H, int32_t F, int32_t E, const void* y_perm,
+                     int32_t y_dtype) {
     if (T < 0 || K <= 0 || E <= 0 || H <= 0 || F <= 0 || K > E || (int64_t)T * K > INT32_MAX)
         return MOE_ERR_INVALID_ARG;
     if (!w || !offsets || (T > 0 && (!x || !perm || !y_perm))) return MOE_ERR_INVALID_ARG;
@@ -259,6 +263,17 @@ moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, 
             !aligned16(y_perm))
             return MOE_ERR_UNSUPPORTED;
     }
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_ffn(const void* x, int32_t x_dtype, const moe_expert_weights* w, const int32_t* offsets,
+                   const int32_t* perm, int32_t T, int32_t K, int32_t H, int32_t F, int32_t E, void* y_perm,
+                   int32_t y_dtype, void* workspace, size_t ws_bytes, moe_stream stream) {
+    const moe_status chk = ffn_check(x, x_dtype, w, offsets, perm, T, K, H, F, E, y_perm, y_dtype);
+    if (chk != MOE_OK) return chk;
     const size_t need = moe_ffn_workspace_size(T, K, E, H, F, x_dtype, w->dtype);
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
     return hip_status(launch_ffn(x, x_dtype, w->dtype, w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down,
@@ -289,6 +304,62 @@ moe_status moe_combine_steer(const void* y_perm, int32_t y_dtype, const int32_t*
         return MOE_ERR_UNSUPPORTED;
     return hip_status(launch_combine_steer(y_perm, y_dtype == MOE_BF16, inv_perm, topk_w, residual, steer_v, T, K, H,
                                            out, out_dtype == MOE_BF16, S(stream)));
+}
+
+size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t K, int32_t F, int32_t x_dtype,
+                                int32_t w_dtype) {
+    if (T < 0 || H <= 0 || E <= 0 || K <= 0 || F <= 0) return 0;
+    const size_t separate = round256(moe_route_group_workspace_size(T, H, E, K, x_dtype)) +
+                            round256(moe_ffn_workspace_size(T, K, E, H, F, x_dtype, w_dtype)) +
+                            round256((size_t)T * K * H * (x_dtype == MOE_F32 ? 4 : 2));
+    const size_t fused = verify_layer_eligible(T, H, E, K, F, x_dtype, w_dtype)
+                             ? round256(verify_layer_workspace_bytes(T, H, E, K, F))
+                             : 0;
+    return separate > fused ? separate : fused;
+}
+
+moe_status moe_layer(const void* x, int32_t x_dtype, const float* w_router, const float* bias,
+                     const moe_expert_weights* w, int32_t T, int32_t H, int32_t E, int32_t K, int32_t F,
+                     const void* residual, const float* steer_v, void* out, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace,
+                     size_t ws_bytes, moe_stream stream) {
+    moe_status chk = route_check(x, x_dtype, w_router, T, H, E, K, topk_idx, topk_w);
+    if (chk != MOE_OK) return chk;
+    if (!counts || !offsets || (T > 0 && (!perm || !inv_perm || !out))) return MOE_ERR_INVALID_ARG;
+    if (!w || !w->w_gate || !w->w_up || !w->w_down || F <= 0) return MOE_ERR_INVALID_ARG;
+    const bool quant = w->dtype == MOE_INT4_B32 || w->dtype == MOE_INT3_B32 || w->dtype == MOE_INT2_B32;
+    if (quant && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    const int32_t ydt = x_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+    const bool fused = T > 0 && verify_layer_eligible(T, H, E, K, F, x_dtype, w->dtype) && aligned16(x) &&
+                       aligned16(w->w_gate) && aligned16(w->w_up) && aligned16(w->w_down) &&
+                       (!quant || (aligned16(w->s_gate) && aligned16(w->s_up) && aligned16(w->s_down)));
+    // otherwise the separate path's checks (the expert call's, on a stand-in y_perm)
+    if (!fused) {
+        chk = ffn_check(x, x_dtype, w, offsets, perm, T, K, H, F, E, workspace, ydt);
+        if (chk != MOE_OK) return chk;
+    }
+    if (H % 8 != 0 || !aligned16(residual) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+    if (steer_v && (H > STEER_MAX_H || !aligned16(steer_v))) return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe_layer_workspace_size(T, H, E, K, F, x_dtype, w->dtype);
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    hipStream_t st = S(stream);
+    if (fused)
+        return hip_status(launch_verify_layer(x, w_router, bias, w->dtype, w->w_gate, w->w_up, w->w_down, w->s_gate,
+                                              w->s_up, w->s_down, T, H, E, K, F, residual, steer_v, out, topk_idx,
+                                              topk_w, counts, offsets, perm, inv_perm, workspace, st));
+    // the separate calls: routing + grouping, experts into y_perm, combine
+    const size_t rg = round256(moe_route_group_workspace_size(T, H, E, K, x_dtype));
+    const size_t fw = round256(moe_ffn_workspace_size(T, K, E, H, F, x_dtype, w->dtype));
+    char* wb = (char*)workspace;
+    void* y = wb + rg + fw;
+    moe_status s = route_group_on(x, x_dtype, w_router, bias, T, H, E, K, topk_idx, topk_w, counts, offsets, perm,
+                                  inv_perm, wb, rg, stream);
+    if (s != MOE_OK) return s;
+    s = moe_ffn(x, x_dtype, w, offsets, perm, T, K, H, F, E, y, ydt, wb + rg, fw, stream);
+    if (s != MOE_OK) return s;
+    if (steer_v) return moe_combine_steer(y, ydt, inv_perm, topk_w, residual, steer_v, T, K, H, out, x_dtype, stream);
+    return moe_combine(y, ydt, inv_perm, topk_w, residual, T, K, H, out, x_dtype, stream);
 }
 
 moe_status moe_expert_freq(const float* logits, int32_t L, int64_t T, int32_t E, int32_t K, int64_t* counts,

@@ -32,6 +32,16 @@ MOE_DEV float fp16_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// A block barrier that orders LDS accesses only: the waves' outstanding global
+// loads stay in flight across it (__syncthreads' workgroup release would wait
+// for them, e.g. for a weight prefetch issued just before).  Use it where
+// only LDS data is exchanged between the waves of a block.
+MOE_DEV void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ wave helpers
 MOE_DEV int lane_id() { return __lane_id(); }
 
@@ -108,6 +118,19 @@ MOE_DEV uint32_t wave_max_u32(uint32_t v) {
 
 MOE_DEV float order_key_value(uint32_t h) { return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h); }
 
+// The order keys of a row of E logits, kv[j] for expert lane + 64 j (0 past
+// E).  Every load is unconditional (past E they re-read the last logit) so
+// all VPL are in flight together: a guarded load would wait for each in turn.
+template <int VPL>
+MOE_DEV void load_order_keys(const float* __restrict__ row, int E, uint32_t (&kv)[VPL]) {
+    const int l = lane_id();
+    float v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; j++) v[j] = row[min(l + j * WAVE, E - 1)];
+#pragma unroll
+    for (int j = 0; j < VPL; j++) kv[j] = l + j * WAVE < E ? f32_order_key(v[j]) : 0u;
+}
+
 // Top-`rounds` under (value desc, expert asc) of the order keys kv[j] of expert
 // e = lane + 64 j (0 = absent; every finite or infinite logit has a key > 0):
 // lane r < rounds receives round r's key and expert.  Per round: the lane
@@ -123,13 +146,13 @@ MOE_DEV void select_top(uint32_t (&kv)[VPL], int rounds, uint32_t& my_key, int& 
 #pragma unroll
         for (int j = 1; j < VPL; j++) m = max(m, kv[j]);
         const uint32_t M = wave_max_u32(m);
-        int win = -1;
+        // the lowest expert holding M: the lowest j whose ballot is not empty,
+        // its lowest lane (scalar selects, no branches)
+        int win = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < VPL; j++) {
-            if (win < 0) {
-                const unsigned long long bm = __ballot(kv[j] == M);
-                if (bm) win = (__ffsll((long long)bm) - 1) + j * WAVE;
-            }
+        for (int j = VPL - 1; j >= 0; j--) {
+            const unsigned long long bm = __ballot(kv[j] == M);
+            win = bm ? (__ffsll((long long)bm) - 1) + j * WAVE : win;
         }
 #pragma unroll
         for (int j = 0; j < VPL; j++) kv[j] = (l + j * WAVE == win) ? 0u : kv[j];
@@ -138,6 +161,58 @@ MOE_DEV void select_top(uint32_t (&kv)[VPL], int rounds, uint32_t& my_key, int& 
             my_e = win;
         }
     }
+}
+
+// select_top's result (lane r < K: rank r's key and expert) by a cut, for
+// latency: tau = the K-th largest of the 64 lane maxima (one lane per round,
+// single values), then every key >= tau is a candidate -- the K lanes with
+// the largest maxima hold K keys >= tau, so the K-th largest key is >= tau
+// and the whole top K is among the candidates -- and each candidate's rank is
+// the number of candidates ahead of it under (key desc, expert asc).  cand
+// (64 entries) and outb (K entries) are the wave's LDS scratch.  Returns
+// false, touching nothing the caller uses, when more than 64 keys reach tau
+// (ties at the cut); then select_top gives the answer.  K <= 64.
+template <int VPL>
+MOE_DEV bool select_top_cut(const uint32_t (&kv)[VPL], int K, uint2* __restrict__ cand, uint2* __restrict__ outb,
+                            uint32_t& my_key, int& my_e) {
+    const int l = lane_id();
+    uint32_t mm = kv[0];
+#pragma unroll
+    for (int j = 1; j < VPL; j++) mm = max(mm, kv[j]);
+    uint32_t tau = 0;
+    for (int r = 0; r < K; r++) {
+        const uint32_t M = wave_max_u32(mm);
+        tau = M;
+        const unsigned long long bm = __ballot(mm == M);
+        mm = l == (__ffsll((long long)bm) - 1) ? 0u : mm;
+    }
+    unsigned long long bj[VPL];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) {
+        bj[j] = __ballot(kv[j] >= tau && kv[j] != 0u);
+        c += __popcll(bj[j]);
+    }
+    if (c > WAVE) return false;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) {
+        if (kv[j] >= tau && kv[j] != 0u)
+            cand[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bj[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bj[j], 0))] =
+                make_uint2(kv[j], (uint32_t)(l + j * WAVE));
+        base += __popcll(bj[j]);
+    }
+    const uint2 me = cand[min(l, c - 1)];
+    int rank = 0;
+    for (int i = 0; i < c; i++) {
+        const uint2 o = cand[i];
+        rank += (o.x > me.x) | ((o.x == me.x) & (o.y < me.y));
+    }
+    if (l < c && rank < K) outb[rank] = me;
+    const uint2 mine = outb[min(l, K - 1)];
+    my_key = l < K ? mine.x : 0u;
+    my_e = l < K ? (int)mine.y : 0;
+    return true;
 }
 
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -80,3 +80,13 @@ hipError_t launch_combine_steer(const void* y, int y_bf16, const int32_t* inv, c
 // freq.hip
 hipError_t launch_freq(const float* logits, int L, int64_t T, int E, int K, unsigned long long* counts,
                        int accumulate, int keep, int32_t* rank_of, int32_t* keep_map, hipStream_t st);
+
+// verify.hip: one whole layer for a few tokens (logits, routing + grouping +
+// gate/up, down + combine; + the projection of a steered layer)
+bool verify_layer_eligible(int T, int H, int E, int K, int F, int x_dtype, int w_dtype);
+size_t verify_layer_workspace_bytes(int T, int H, int E, int K, int F);
+hipError_t launch_verify_layer(const void* x, const float* wr, const float* bias, int w_dtype, const void* wg,
+                               const void* wu, const void* wd, const void* sg, const void* su, const void* sd, int T,
+                               int H, int E, int K, int F, const void* residual, const float* steer_v, void* out,
+                               int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                               void* ws, hipStream_t st);

@@ -413,11 +413,7 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     const int l = lane_id();
     const float* row = logits + (long)t * E;
     uint32_t kv[VPL];
-#pragma unroll
-    for (int j = 0; j < VPL; j++) {
-        const int e = l + j * WAVE;
-        kv[j] = e < E ? f32_order_key(row[e]) : 0u;
-    }
+    load_order_keys<VPL>(row, E, kv);
     if (!exact) {
         float xs = 0.f, wm = 0.f;
         const uint4* xr = reinterpret_cast<const uint4*>(xb + (long)t * H);
@@ -485,11 +481,7 @@ __global__ __launch_bounds__(1024) void k_route_select_group(const float* __rest
         const int t = wave;
         const float* row = logits + (long)t * E;
         uint32_t kv[VPL];
-#pragma unroll
-        for (int j = 0; j < VPL; j++) {
-            const int e = l + j * WAVE;
-            kv[j] = e < E ? f32_order_key(row[e]) : 0u;
-        }
+        load_order_keys<VPL>(row, E, kv);
         uint32_t key;
         int sel_i;
         select_top<VPL>(kv, K, key, sel_i);
@@ -593,16 +585,19 @@ __global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict
 #pragma unroll
     for (int i = 0; i < HL; i++) wf[i] = wr[(long)er * H + l + i * WAVE];   // H == 64 * HL
     const float b = bias ? bias[er] : 0.f;
+    // x [T][H] into LDS, 16 chunks of 16 bytes per thread in flight at a time
+    // (past the end the last chunk is loaded and stored again)
     const int per = 16 / (int)sizeof(XT);
     const int nchunk = T * H / per;
     const uint4* xg = reinterpret_cast<const uint4*>(x);
     uint4* xd = reinterpret_cast<uint4*>(xs);
-    int i0 = tid;
-    for (; i0 + 3 * 128 < nchunk; i0 += 4 * 128) {
-        const uint4 a0 = xg[i0], a1 = xg[i0 + 128], a2 = xg[i0 + 256], a3 = xg[i0 + 384];
-        xd[i0] = a0; xd[i0 + 128] = a1; xd[i0 + 256] = a2; xd[i0 + 384] = a3;
+    for (int c0 = 0; c0 * 128 < nchunk; c0 += 16) {
+        uint4 a[16];
+#pragma unroll
+        for (int c = 0; c < 16; c++) a[c] = xg[min(tid + (c0 + c) * 128, nchunk - 1)];
+#pragma unroll
+        for (int c = 0; c < 16; c++) xd[min(tid + (c0 + c) * 128, nchunk - 1)] = a[c];
     }
-    for (; i0 < nchunk; i0 += 128) xd[i0] = xg[i0];
     __syncthreads();
     if (e >= E) return;
     double w[HL];

@@ -19,7 +19,7 @@ _QUANT_BY_BITS = {4: INT4_B32, 3: INT3_B32, 2: INT2_B32}
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_ffn_workspace_size", "moe_ffn",
-           "moe_route_group_workspace_size", "moe_route_group", "moe_route_group_noalloc", "moe_combine", "moe_combine_steer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
+           "moe_route_group_workspace_size", "moe_route_group", "moe_route_group_noalloc", "moe_combine", "moe_combine_steer", "moe_layer_workspace_size", "moe_layer", "moe_expert_freq", "moe_profile_workspace_size", "moe_profile_rank",
            "moe_profile_hits", "moe_strp_size", "moe_strp_write", "moe_strp_read", "moe_profile_remap"]
 
 
@@ -79,6 +79,11 @@ def load():
     L.moe_route_group_noalloc.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine_steer.restype = ctypes.c_int
     L.moe_combine_steer.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp]
+    L.moe_layer_workspace_size.restype = sz
+    L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.moe_layer.restype = ctypes.c_int
+    L.moe_layer.argtypes = [vp, i32, vp, vp, ctypes.POINTER(ExpertWeights), i32, i32, i32, i32, i32, vp, vp, vp,
+                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_freq.restype = ctypes.c_int
     L.moe_expert_freq.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, vp, vp, vp]
     L.moe_profile_workspace_size.restype = sz
@@ -433,12 +438,19 @@ def profile_remap(pairs, keep_map, E_old: int):
 
 
 # ------------------------------------------------------------------ one whole layer
+def layer_workspace_size(T, H, E, K, F, x_dtype=BF16, w_dtype=BF16) -> int:
+    return int(load().moe_layer_workspace_size(T, H, E, K, F, x_dtype, w_dtype))
+
+
 class LayerWorkspace:
-    """Preallocated workspaces and outputs for repeated calls of `layer` at one shape."""
+    """Preallocated workspaces and outputs for repeated calls of `layer` at one shape
+    (and of the separate calls at that shape)."""
 
     def __init__(self, T, H, E, K, F, x_dtype=torch.bfloat16, w_dtype=BF16, y_dtype=None, device="cuda"):
         xd = F32 if x_dtype == torch.float32 else BF16
         self.y_dtype = y_dtype or x_dtype
+        self.layer_ws = torch.empty(layer_workspace_size(T, H, E, K, F, xd, w_dtype), dtype=torch.uint8,
+                                    device=device)
         self.route_ws = torch.empty(route_workspace_size(T, H, E, K, xd), dtype=torch.uint8, device=device)
         self.group_ws = torch.empty(route_group_workspace_size(T, H, E, K, xd), dtype=torch.uint8, device=device)
         self.perm_ws = torch.empty(permute_workspace_size(T, K, E), dtype=torch.uint8, device=device)
@@ -453,16 +465,37 @@ class LayerWorkspace:
 
 def layer(x, w_router, wg, wu, wd, K: int, bias=None, sg=None, su=None, sd=None, residual=None, lw=None,
           stream=None, out=None, steer_v=None):
-    """route + permute (one call, moe_route_group) -> ffn -> combine (steered
-    if steer_v is given) for one MoE layer.  Returns (out, routing dict)."""
+    """One MoE layer in one library call (moe_layer): routing + grouping, the
+    experts and the combine (steered if steer_v is given).  Returns (out,
+    routing dict)."""
+    _need(x, "x")
     T, H = x.shape
     E, F = wg.shape[0], wg.shape[1]
-    idx, w, counts, offsets, perm, inv = route_group(
-        x, w_router, K, bias=bias, workspace=lw.group_ws if lw else None, stream=stream,
-        out=(lw.route_out + lw.perm_out) if lw else None)
-    y = ffn(x, wg, wu, wd, offsets, perm, K, sg, su, sd, y_dtype=lw.y_dtype if lw else None,
-            out=lw.y if lw else None, workspace=lw.ffn_ws if lw else None, stream=stream)
-    if out is None and lw is not None:
-        out = lw.out
-    o = combine(y, inv, w, residual=residual, out_dtype=x.dtype, out=out, stream=stream, steer_v=steer_v)
-    return o, dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, y=y)
+    _need(w_router, "w_router", torch.float32, (E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    if residual is not None:
+        _need(residual, "residual", x.dtype, (T, H))
+    if steer_v is not None:
+        _need(steer_v, "steer_v", torch.float32, (H,))
+    ws_struct = weights_struct(wg, wu, wd, sg, su, sd)
+    dev = x.device
+    if lw is not None:
+        idx, w = lw.route_out
+        counts, offsets, perm, inv = lw.perm_out
+        if out is None:
+            out = lw.out
+    else:
+        i32 = dict(dtype=torch.int32, device=dev)
+        idx, w = torch.empty((T, K), **i32), torch.empty((T, K), dtype=torch.float32, device=dev)
+        counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+        perm, inv = torch.empty(T * K, **i32), torch.empty(T * K, **i32)
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    _need(out, "out", x.dtype, (T, H))
+    nb = layer_workspace_size(T, H, E, K, F, _act_dtype(x), ws_struct.dtype)
+    ws = _workspace(nb, dev, lw.layer_ws if lw is not None else None)
+    _chk(load().moe_layer(_ptr(x), _act_dtype(x), _ptr(w_router), _ptr(bias), ctypes.byref(ws_struct), T, H, E, K, F,
+                          _ptr(residual), _ptr(steer_v), _ptr(out), _ptr(idx), _ptr(w), _ptr(counts), _ptr(offsets),
+                          _ptr(perm), _ptr(inv), _ptr(ws), nb, _stream(stream)), "moe_layer")
+    return out, dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv)

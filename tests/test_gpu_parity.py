@@ -30,16 +30,26 @@ def gpu():
     torch.cuda.synchronize()
 
 
-def run_layer(d, residual=None, y_dtype=None):
+def run_layer(d, residual=None, steer_v=None):
+    """The layer in one call (moe_layer)."""
     s = d.shape
     lw = moe.LayerWorkspace(s.T, s.H, s.E, s.K, s.F, x_dtype=d.x.dtype,
                             w_dtype={"f32": moe.F32, "bf16": moe.BF16, "int4": moe.INT4_B32, "int3": moe.INT3_B32,
-                                     "int2": moe.INT2_B32}[s.wdt],
-                            y_dtype=y_dtype)
+                                     "int2": moe.INT2_B32}[s.wdt])
     out, r = moe.layer(d.x, d.wr, d.wg, d.wu, d.wd, s.K, bias=d.bias, sg=d.sg, su=d.su, sd=d.sd,
-                       residual=residual, lw=lw)
+                       residual=residual, lw=lw, steer_v=steer_v)
     torch.cuda.synchronize()
     return out, r
+
+
+def run_separate(d, residual=None, y_dtype=None, steer_v=None):
+    """The layer as the separate calls: route + group, experts into y_perm (y_dtype), combine."""
+    s = d.shape
+    idx, w, counts, offsets, perm, inv = moe.route_group(d.x, d.wr, s.K, bias=d.bias)
+    y = moe.ffn(d.x, d.wg, d.wu, d.wd, offsets, perm, s.K, d.sg, d.su, d.sd, y_dtype=y_dtype or d.x.dtype)
+    out = moe.combine(y, inv, w, residual=residual, out_dtype=d.x.dtype, steer_v=steer_v)
+    torch.cuda.synchronize()
+    return out, dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, y=y)
 
 
 def check_routing_and_grouping(r, ref_idx, ref_w, E):
@@ -115,9 +125,76 @@ def test_small_layers_span_tiles(s):
     torch.cuda.synchronize()
     assert np.array_equal(to_host(lg).view(np.uint32), ref_lg.view(np.uint32))
     assert np.array_equal(to_host(idx2), ref_idx)
-    # fp32 y_perm gives the same routing and an in-tolerance output
-    out32, _ = run_layer(d, y_dtype=torch.float32)
-    assert row_rel_err(to_host(out32), ref_out) <= TOL_BF16
+    # the separate calls, with a bf16 and an fp32 y_perm: the same routing and in-tolerance outputs
+    for y_dtype in (None, torch.float32):
+        out_s, r_s = run_separate(d, y_dtype=y_dtype)
+        check_routing_and_grouping(r_s, ref_idx, ref_w, s.E)
+        assert row_rel_err(to_host(out_s), ref_out) <= TOL_BF16
+
+
+# one whole layer for a few tokens in three launches (moe_layer's fused path:
+# T <= 8, H 2048, F 512): (T, E, K, weights, Zipf offset, residual, steering)
+FUSED = [
+    (1, 64, 10, "bf16", False, False, False),
+    (5, 64, 10, "int4", True, True, False),
+    (8, 16, 16, "bf16", True, True, True),      # T*K = 128, up to 8 rows per expert
+    (3, 40, 4, "int3", False, False, True),
+    (7, 24, 8, "int2", True, True, False),
+    (6, 9, 9, "int4", False, False, False),     # K = E: every expert in every token
+    (4, 33, 1, "bf16", False, True, False),     # K = 1
+]
+
+
+@pytest.mark.parametrize("T,E,K,wdt,zipf,with_res,steer", FUSED,
+                         ids=lambda v: str(v) if not isinstance(v, bool) else ("y" if v else "n"))
+def test_layer_few_tokens_fused(T, E, K, wdt, zipf, with_res, steer):
+    """moe_layer for a few tokens (selection and grouping inside the gate/up
+    launch, the combine inside the down launch): routing and grouping exact
+    and identical to the separate calls, the output (in place on the residual
+    stream, optionally steered) within the bf16 bound of the oracle."""
+    from oracle import steer as steer_oracle
+    s = synth.LayerShape(T=T, H=2048, E=E, K=K, F=512, act="bf16", wdt=wdt, zipf=zipf)
+    h = synth.make_host_layer(s, seed=T + E, cfg=9)
+    d = device_from_host(h)
+    ref_idx, ref_w, _ = oracle.route(h.x, h.wr, s.K, h.bias)
+    v = torch.from_numpy(synth.steer_vector(s.H, layer=T)).cuda() if steer else None
+    if with_res:
+        stream = d.x.clone()
+        lw = moe.LayerWorkspace(T, s.H, E, K, s.F, w_dtype={"bf16": moe.BF16, "int4": moe.INT4_B32,
+                                                            "int3": moe.INT3_B32, "int2": moe.INT2_B32}[wdt])
+        out, r = moe.layer(stream, d.wr, d.wg, d.wu, d.wd, K, bias=d.bias, sg=d.sg, su=d.su, sd=d.sd,
+                           residual=stream, lw=lw, out=stream, steer_v=v)
+        torch.cuda.synchronize()
+    else:
+        out, r = run_layer(d, steer_v=v)
+    check_routing_and_grouping(r, ref_idx, ref_w, E)
+    _, r_sep = run_separate(d)
+    for k in ("idx", "w", "counts", "offsets", "perm", "inv"):
+        assert torch.equal(r[k], r_sep[k]), f"{k} differs from the separate calls"
+    res = h.x if with_res else None
+    if steer:
+        _, yk = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d), want_y=True)
+        hh = (ref_w.astype(np.float64)[:, :, None] * yk).sum(axis=1) + (as_f64(h.x) if with_res else 0.0)
+        ref_out = steer_oracle.project_out(hh, to_host(v).astype(np.float64))
+    else:
+        ref_out = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d), residual=res)
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
+def test_layer_few_tokens_fused_many_experts_and_ties():
+    """The fused path's selection over more than 512 experts (16 logits per
+    lane), with exact logit ties (duplicated router rows: the lower id wins)."""
+    s = synth.LayerShape(T=8, H=2048, E=700, K=10, F=512, act="bf16", wdt="bf16")
+    d = synth.make_device_layer(s, seed=2, cfg=9, layer=0, device="cuda")
+    d.wr[1::7] = d.wr[0::7][: d.wr[1::7].shape[0]]          # pairs of equal router rows
+    torch.cuda.synchronize()
+    x, wr = to_host(d.x), to_host(d.wr)
+    ref_idx, ref_w, ref_lg = oracle.route(x, wr, s.K)
+    assert np.any(np.diff(np.sort(ref_lg, axis=1), axis=1) == 0)
+    out, r = run_layer(d)
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    ref_out = oracle.layer_rows(x, ref_idx, ref_w, host_weights(d))
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
 
 
 @pytest.mark.parametrize("wdt", ["bf16", "int4"])
@@ -152,7 +229,7 @@ def test_gemm_path_blocks_walk_several_items(wdt):
     rows = np.unique(np.concatenate([[0, s.T - 1], np.random.default_rng(1).choice(s.T, 62, replace=False)]))
     ref_out = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d), rows=rows)
     for y_dtype in (None, torch.float32):
-        out, r = run_layer(d, y_dtype=y_dtype)
+        out, r = run_separate(d, y_dtype=y_dtype)
         check_routing_and_grouping(r, ref_idx, ref_w, s.E)
         assert row_rel_err(to_host(out)[rows], ref_out) <= TOL_BF16
 
