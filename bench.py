@@ -587,6 +587,8 @@ def main():
                         "prefill chunk 8192 tok, E512 top-10 bf16, Zipf(1.1) router offset", stat_runs=20)
         r["roofline"] = ffn_mfma_roofline(r)
         r["unit"] = "tokens/s"
+        r["steps_rule"] = ("--steps / 10 (at least 8) timed steps after 4 warmup steps: a step is ~1 ms, and only the "
+                           "headline workload takes --steps and --warmup as given")
         if cpu:
             r["cpu_baseline"] = cpu_baseline_prefill(torch, r["_layers"][0])
         log(f"[prefill] {r['ms_per_step']:.3f} ms/step, separate calls {r['separate_calls_us']}")
@@ -595,6 +597,7 @@ def main():
         torch.cuda.empty_cache()
     if "freq" in wl:
         r, prof = bench_freq(torch, moe, synth, max(5, steps // 20), 2, use_graph, cpu)
+        r["steps_rule"] = "--steps / 20 (at least 5) calls after 2 warmup calls: a call reads 25.8 GB (~4 ms)"
         log(f"[freq] {r['ms_per_step']:.3f} ms/step")
         also.append(r)
         also.append(prof)
@@ -610,6 +613,7 @@ def main():
         for shp, nm in ((synth.STACK_INT4_VERIFY, "pruned 48-layer int4 stack, 5-tok verify"),
                         (synth.STACK_INT4_PREFILL, "pruned 48-layer int4 stack, 8192-tok prefill")):
             r = bench_stack(torch, moe, synth, shp, max(3, steps // 40), 1, use_graph, nm, cpu=cpu)
+            r["steps_rule"] = "--steps / 40 (at least 3) steps after 1 warmup step: a step is 48 layers (2-42 ms)"
             log(f"[stack T={shp.T}] {r['ms_per_step']:.3f} ms/step, {r['ms_per_step_steered']:.3f} ms steered")
             also.append(r)
             torch.cuda.empty_cache()
