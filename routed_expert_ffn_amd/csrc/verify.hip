@@ -379,13 +379,15 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
 
 namespace {
 // The touched list held in registers by every wave: lane j keeps entries j
-// and j + 64 (entries past nlist repeat the last), read back wave-uniformly.
+// and j + 64, read back wave-uniformly.  The loads are clamped to the list's
+// capacity (T*K entries), not to its length, so they need not wait for the
+// length; entries past the length are never read back.
 struct WaveList {
     int4 a, b;
-    MOE_DEV void load(const int4* __restrict__ g_list, int nlist) {
+    MOE_DEV void load(const int4* __restrict__ g_list, int cap) {
         const int l = lane_id();
-        a = g_list[min(l, nlist - 1)];
-        b = g_list[min(l + WAVE, nlist - 1)];
+        a = g_list[min(l, cap - 1)];
+        b = g_list[min(l + WAVE, cap - 1)];
     }
     MOE_DEV int x(int j) const {
         return j < WAVE ? __builtin_amdgcn_readlane(a.x, j) : __builtin_amdgcn_readlane(b.x, j - WAVE);
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(512) void k_vdown(const uint16_t* __restrict__ abuf
     const int nlist = __builtin_amdgcn_readfirstlane(*g_nlist);
     const int h = blockIdx.x * 8 + wave;          // grid = H / 8: every row exists
     WaveList lst;
-    lst.load(g_list, nlist);
+    lst.load(g_list, n);
     DownStage<MS> stg;
     stg.load(abuf, n, topk_w, inv);
     float* yw = ys + wave * n;
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(512) void k_vdown_q(const uint16_t* __restrict__ ab
     float* yr = ys + rloc * n;
     const int n_items = nlist > q ? (nlist - q + 3) / 4 : 0;
     WaveList lst;
-    lst.load(g_list, nlist);
+    lst.load(g_list, n);
     DownStage<MS> stg;
     stg.load(abuf, n, topk_w, inv);
     constexpr int QW = QWords<QB>::n;
