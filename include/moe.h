@@ -106,7 +106,7 @@ const char* moe_status_string(moe_status s);
  *   topk_idx   [T][K] int32 out: the K largest logits, in descending order,
  *              ties to the lower expert id.
  *   topk_w     [T][K] fp32 out: exp(l_k - l_0) / sum_j exp(l_j - l_0) over the
- *              K selected.
+ *              K selected, fp32, the sum taken in rank order j = 0, 1, ...
  *   logits_out [T][E] fp32 out, or NULL.
  * Logits are fp32(S + 0) then + bias in fp32, S the fp64 sum of the exact
  * products x*w taken in wave-64 order (64 strided partial sums, then a pairwise

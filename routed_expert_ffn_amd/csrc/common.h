@@ -116,6 +116,18 @@ MOE_DEV uint32_t wave_max_u32(uint32_t v) {
     return max(max(a, b), max(c, d));
 }
 
+// Softmax weights of a wave's selection (lane k < K holds the k-th largest
+// value v): exp(v - v_0) / sum_k exp(v_k - v_0), the sum taken in rank order
+// (k = 0, 1, ...) from register reads, the same value in every lane.
+MOE_DEV float selection_weight(float v, int K) {
+    const int l = lane_id();
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float ex = l < K ? expf(v - v0) : 0.0f;
+    float sum = 0.0f;
+    for (int k = 0; k < K; k++) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), k));
+    return ex / sum;
+}
+
 MOE_DEV float order_key_value(uint32_t h) { return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h); }
 
 // The order keys of a row of E logits, kv[j] for expert lane + 64 j (0 past
@@ -202,11 +214,16 @@ MOE_DEV bool select_top_cut(const uint32_t (&kv)[VPL], int K, uint2* __restrict_
                 make_uint2(kv[j], (uint32_t)(l + j * WAVE));
         base += __popcll(bj[j]);
     }
+    // candidate i in lane i; its rank = the candidates ahead of it in (key
+    // descending, expert ascending) order: one 64-bit compare of packed
+    // (key, ~expert) per candidate, each read from its lane's registers
     const uint2 me = cand[min(l, c - 1)];
+    const uint64_t pm = ((uint64_t)me.x << 32) | (uint32_t)~me.y;
     int rank = 0;
     for (int i = 0; i < c; i++) {
-        const uint2 o = cand[i];
-        rank += (o.x > me.x) | ((o.x == me.x) & (o.y < me.y));
+        const uint64_t po = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)me.x, i) << 32) |
+                            (uint32_t)~(uint32_t)__builtin_amdgcn_readlane((int)me.y, i);
+        rank += po > pm;
     }
     if (l < c && rank < K) outb[rank] = me;
     const uint2 mine = outb[min(l, K - 1)];

@@ -380,14 +380,10 @@ MOE_DEV unsigned long long select_rounds(unsigned long long (&k)[VPL], int round
 MOE_DEV void write_selection(float sel_v, int sel_i, int K, long t, int32_t* __restrict__ idx_out,
                              float* __restrict__ w_out) {
     const int l = lane_id();
-    const float v0 = __shfl(sel_v, 0, WAVE);
-    const float ex = (l < K) ? expf(sel_v - v0) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
+    const float w = selection_weight(sel_v, K);
     if (l < K) {
         idx_out[t * K + l] = sel_i;
-        w_out[t * K + l] = ex / sum;
+        w_out[t * K + l] = w;
     }
 }
 

@@ -52,18 +52,11 @@ struct VerifyOut {
 // computes them; lane r < K ends with rank r's expert and weight.
 template <int VPL>
 MOE_DEV void select_weights(uint32_t (&kv)[VPL], int K, uint2* __restrict__ scratch, int& e_out, float& w_out) {
-    const int l = lane_id();
     uint32_t key;
     int sel;
     if (!select_top_cut<VPL>(kv, K, scratch, scratch + WAVE, key, sel)) select_top<VPL>(kv, K, key, sel);
-    const float v = order_key_value(key);
-    const float v0 = __shfl(v, 0, WAVE);
-    const float ex = l < K ? expf(v - v0) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
     e_out = sel;
-    w_out = ex / sum;
+    w_out = selection_weight(order_key_value(key), K);
 }
 
 // Calls f(u, v[u]) for u < n rounded up to 16, over an LDS array v of
@@ -91,79 +84,87 @@ MOE_DEV void for_slots(const int* __restrict__ v, int n, Fn&& f) {
 // Routing and grouping of T <= 8 tokens inside one block of 8 waves (every
 // block of the gate/up launch runs it): wave t selects token t from the order
 // keys it loaded (kv, see the kernels); then the T*K slots are grouped by
-// expert, stable by slot: the grouped row of slot s is the number of slots
-// with a lower expert plus the earlier slots with the same expert.  The
-// touched experts become (expert, first grouped row, rows) in expert order.
-// The writer block also stores the routing and grouping outputs and the
-// touched list.  Needs T <= 8 and T*K <= VMAX_SLOTS <= blockDim.x; returns
-// the number of touched experts.  LDS: sel, first [VMAX_SLOTS] int (16-byte
-// aligned); list [T*K] int4; prow [T*K] int (token of every grouped row);
-// sscratch [8 waves][128] uint2 (the selection's scratch).
+// expert, stable by slot: the grouped row of slot s is its rank in (expert,
+// slot) order, counted by the waves that hold slots only (one compare of
+// packed keys e * VMAX_SLOTS + s per slot).  Group starts over the sorted rows
+// become two 64-bit ballots, from which every touched expert's list index and
+// row count follow by population counts.  The writer block also stores the
+// routing and grouping outputs (counts and offsets by a binary search of each
+// expert in the touched list).  Needs T <= 8 and T*K <= VMAX_SLOTS <=
+// blockDim.x; returns the number of touched experts.  LDS: sel, srt
+// [VMAX_SLOTS] int (16-byte aligned; slot keys, sorted keys); list [T*K] int4
+// (expert, first grouped row, rows), expert order; prow [T*K] int (token of
+// every grouped row); sscratch [8 waves][128] uint2 (the selection's scratch).
 template <int VPL>
 MOE_DEV int route_group_block(uint32_t (&kv)[VPL], int T, int E, int K, int* __restrict__ sel,
-                              int* __restrict__ first, int4* __restrict__ list, int* __restrict__ prow,
+                              int* __restrict__ srt, int4* __restrict__ list, int* __restrict__ prow,
                               uint2* __restrict__ sscratch, bool writer, const VerifyOut& o) {
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    const int n = T * K;
     if (wave < T) {
         int e;
         float w;
         select_weights<VPL>(kv, K, sscratch + wave * 2 * WAVE, e, w);
         if (l < K) {
-            sel[wave * K + l] = e;
+            sel[wave * K + l] = e * VMAX_SLOTS + wave * K + l;
             if (writer) {
                 o.idx[wave * K + l] = e;
                 o.w[wave * K + l] = w;
             }
         }
     }
-    lds_barrier();
-    const int n = T * K;
     if (tid < VMAX_SLOTS - n) sel[n + tid] = 0x7fffffff;   // padding read by for_slots, never counted
     lds_barrier();
-    const int e = sel[min(tid, n - 1)];
-    int below = 0, before = 0, same = 0;
-    for_slots(sel, n, [&](int u, int eu) __attribute__((always_inline)) {
-        below += eu < e;
-        before += (eu == e) & (u < tid);
-        same += eu == e;
-    });
-    const int pos = below + before;
     if (tid < n) {
+        const int me = sel[tid];
+        int pos = 0;
+        for_slots(sel, n, [&](int, int ku) __attribute__((always_inline)) { pos += ku < me; });
+        srt[pos] = me;
         prow[pos] = tid / K;
-        first[tid] = before == 0 ? e : 0x7fffffff;   // the expert of a slot that starts its group
         if (writer) {
             o.perm[pos] = tid;
             o.inv[tid] = pos;
         }
     }
-    if (tid < VMAX_SLOTS - n) first[n + tid] = 0x7fffffff;
+    if (tid < VMAX_SLOTS - n) srt[n + tid] = 0x7fffffff;
     lds_barrier();
-    int nlist = 0, j = 0;
-    for_slots(first, n, [&](int, int fu) __attribute__((always_inline)) {
-        nlist += fu != 0x7fffffff;
-        j += fu < e;
-    });
-    if (tid < n && before == 0) {
-        const int4 ent = make_int4(e, pos, same, 0);
-        list[j] = ent;
-        if (writer) o.list[j] = ent;
+    // a sorted row starts a group when its expert differs from the row before
+    auto starts = [&](int p) __attribute__((always_inline)) -> bool {
+        return p < n && (p == 0 || (srt[p - 1] / VMAX_SLOTS) != (srt[p] / VMAX_SLOTS));
+    };
+    const uint64_t m0 = __ballot(starts(l)), m1 = __ballot(starts(l + WAVE));
+    const int c0 = __popcll(m0), nlist = c0 + __popcll(m1);
+    if (wave < 2) {
+        const int p = wave * WAVE + l;
+        const uint64_t m = wave ? m1 : m0;
+        if ((m >> l) & 1ull) {
+            const int j = (wave ? c0 : 0) +
+                          (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const uint64_t above = l == WAVE - 1 ? 0ull : m >> (l + 1);
+            const int next = above ? p + 1 + __builtin_ctzll(above) : (wave == 0 && m1) ? WAVE + __builtin_ctzll(m1) : n;
+            const int4 ent = make_int4(srt[p] / VMAX_SLOTS, p, next - p, 0);
+            list[j] = ent;
+            if (writer) o.list[j] = ent;
+        }
     }
+    lds_barrier();
     if (writer) {
         if (tid == 0) {
             *o.nlist = nlist;
             o.offsets[E] = n;
         }
-        for (int x = tid; x < E; x += blockDim.x) {
-            int c = 0, b = 0;
-            for_slots(sel, n, [&](int, int eu) __attribute__((always_inline)) {
-                c += eu == x;
-                b += eu < x;
-            });
-            o.counts[x] = c;
-            o.offsets[x] = b;
+        for (int x = tid; x < E; x += blockDim.x) {   // the first touched expert >= x
+            int lo = 0, hi = nlist;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (list[mid].x < x) lo = mid + 1;
+                else hi = mid;
+            }
+            const bool hit = lo < nlist && list[lo].x == x;
+            o.counts[x] = hit ? list[lo].z : 0;
+            o.offsets[x] = lo < nlist ? list[lo].y : n;
         }
     }
-    lds_barrier();
     return nlist;
 }
 
@@ -222,8 +223,8 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                 // [T][H]
     int4* list = reinterpret_cast<int4*>(smem + (size_t)T * H * 2);   // [n]
     int* sel = reinterpret_cast<int*>(list + n);                      // [VMAX_SLOTS]
-    int* first = sel + VMAX_SLOTS;                                    // [VMAX_SLOTS]
-    uint2* sscr = reinterpret_cast<uint2*>(first + VMAX_SLOTS);       // [8][128]
+    int* srt = sel + VMAX_SLOTS;                                      // [VMAX_SLOTS]
+    uint2* sscr = reinterpret_cast<uint2*>(srt + VMAX_SLOTS);       // [8][128]
     int* prow = reinterpret_cast<int*>(sscr + 8 * 2 * WAVE);          // [n]
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
     // the token rows' loads go out first, then wave t's loads of token t's
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
     xst.store_x(xs, T);
-    const int nlist = route_group_block<VPL>(kv, T, E, K, sel, first, list, prow, sscr, blockIdx.x == 0, o);
+    const int nlist = route_group_block<VPL>(kv, T, E, K, sel, srt, list, prow, sscr, blockIdx.x == 0, o);
 
     const int tpe = F / FR;
     const int n_items = nlist * tpe;
@@ -304,8 +305,8 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
     float* xsum = reinterpret_cast<float*>(smem + (size_t)T * H * 2);      // [T][H/32]
     int4* list = reinterpret_cast<int4*>(xsum + T * (H / 32));             // [n]
     int* sel = reinterpret_cast<int*>(list + n);                           // [VMAX_SLOTS]
-    int* first = sel + VMAX_SLOTS;                                         // [VMAX_SLOTS]
-    uint2* sscr = reinterpret_cast<uint2*>(first + VMAX_SLOTS);            // [8][128]
+    int* srt = sel + VMAX_SLOTS;                                           // [VMAX_SLOTS]
+    uint2* sscr = reinterpret_cast<uint2*>(srt + VMAX_SLOTS);            // [8][128]
     int* prow = reinterpret_cast<int*>(sscr + 8 * 2 * WAVE);               // [n]
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
     // the token rows' loads go out first, then wave t's loads of token t's
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
     xst.store_x(xs, T);
-    const int nlist = route_group_block<VPL>(kv, T, E, K, sel, first, list, prow, sscr, blockIdx.x == 0, o);
+    const int nlist = route_group_block<VPL>(kv, T, E, K, sel, srt, list, prow, sscr, blockIdx.x == 0, o);
 
     const int tpe = F / FR;
     const int n_items = nlist * tpe;
