@@ -27,6 +27,23 @@ MOE_DEV float dot8bf(uint4 w, uint4 x, float c) {
 }
 MOE_DEV float silu_ref(float g) { return g / (1.0f + expf(-g)); }
 
+// The partner's value at distance D of the transposing reduction below.
+// Within a row of 16 lanes it is a DPP move, whose partner pairs lanes across
+// bit D as xor D does (D = 8: lane 15 - i, the row mirror; D = 4: 7 - i within
+// each half row; D = 2, 1: the quad swaps), so every lane keeps the same
+// entries; only which lanes' partial sums meet differs.  Across rows (D = 16,
+// 32) it is a lane permute.
+template <int D>
+MOE_DEV float tr_partner(float x) {
+    if constexpr (D >= 16) {
+        return __shfl_xor(x, D, WAVE);
+    } else {
+        constexpr int ctrl = D == 8 ? 0x140 : D == 4 ? 0x141 : D == 2 ? 0x4E : 0xB1;
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF,
+                                                                     false));
+    }
+}
+
 template <int CNT, int D, int V>
 MOE_DEV void tr_step(float (&v)[V], int l) {
     if constexpr (D >= 1) {
@@ -37,11 +54,11 @@ MOE_DEV void tr_step(float (&v)[V], int l) {
             for (int i = 0; i < half; i++) {
                 const float keep = bit ? v[i + half] : v[i];
                 const float send = bit ? v[i] : v[i + half];
-                v[i] = keep + __shfl_xor(send, D, WAVE);
+                v[i] = keep + tr_partner<D>(send);
             }
             tr_step<half, D / 2, V>(v, l);
         } else {
-            v[0] += __shfl_xor(v[0], D, WAVE);
+            v[0] += tr_partner<D>(v[0]);
             tr_step<1, D / 2, V>(v, l);
         }
     }
