@@ -31,12 +31,22 @@ MOE_DEV float silu_ref(float g) { return g / (1.0f + expf(-g)); }
 // Within a row of 16 lanes it is a DPP move, whose partner pairs lanes across
 // bit D as xor D does (D = 8: lane 15 - i, the row mirror; D = 4: 7 - i within
 // each half row; D = 2, 1: the quad swaps), so every lane keeps the same
-// entries; only which lanes' partial sums meet differs.  Across rows (D = 16,
-// 32) it is a lane permute.
+// entries; only which lanes' partial sums meet differs.  Across rows it is the
+// lane i ^ D exactly: v_permlane16_swap / v_permlane32_swap with both operands
+// x leave row r ^ 1 (half h ^ 1) of x in the first result on odd rows (upper
+// half) and in the second on even rows (lower half).
 template <int D>
 MOE_DEV float tr_partner(float x) {
     if constexpr (D >= 16) {
-        return __shfl_xor(x, D, WAVE);
+        const unsigned u = __builtin_bit_cast(unsigned, x);
+        const bool hi = (lane_id() & D) != 0;
+        if constexpr (D == 32) {
+            const auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            return __builtin_bit_cast(float, hi ? q[0] : q[1]);
+        } else {
+            const auto q = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            return __builtin_bit_cast(float, hi ? q[0] : q[1]);
+        }
     } else {
         constexpr int ctrl = D == 8 ? 0x140 : D == 4 ? 0x141 : D == 2 ? 0x4E : 0xB1;
         return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF,
