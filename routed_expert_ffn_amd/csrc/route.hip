@@ -560,56 +560,109 @@ __global__ __launch_bounds__(256) void k_route_recheck(const float* __restrict__
 
 // ------------------------------------------------------------------ exact logits, few tokens
 
-// One wave per expert, every token: the router row (H fp32) is loaded once into
-// registers (H/64 independent loads per lane in flight); token rows are staged
-// in LDS.  Two experts per block.
+// Two waves per expert, each taking every other token (h, h + 2, ...): the
+// router row (H fp32) is held in registers (H/64 independent loads per lane in
+// flight), the token rows are staged in LDS.  Two experts per block, so a
+// block's four waves fill a CU's four SIMDs.
 constexpr int XS_MAX_T = 16;
+constexpr int XS_GROUP = 4;          // tokens whose partial sums a wave builds together
+
+// Lane j < D receives lane j + D's value (the other lanes' results are not
+// used): the pairings of the exact logit's summation tree, on 64-bit values.
+// D = 32 and 16 cross rows of 16 lanes with the permlane swaps, D = 8 and 4
+// shift within a row (row_shl), D = 2 and 1 are quad permutations.
+template <int D>
+MOE_DEV double lane_down(double v) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
+    if constexpr (D == 32) {
+        lo = __builtin_amdgcn_permlane32_swap(lo, lo, false, false)[1];
+        hi = __builtin_amdgcn_permlane32_swap(hi, hi, false, false)[1];
+    } else if constexpr (D == 16) {
+        lo = __builtin_amdgcn_permlane16_swap(lo, lo, false, false)[1];
+        hi = __builtin_amdgcn_permlane16_swap(hi, hi, false, false)[1];
+    } else {
+        constexpr int ctrl = D == 8 ? 0x108 : D == 4 ? 0x104 : D == 2 ? 0x4E : 0xB1;
+        lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)lo, ctrl, 0xF, 0xF, false);
+        hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)hi, ctrl, 0xF, 0xF, false);
+    }
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Logits of NT tokens t0, t0 + 2, ... for this wave's expert: the strided
+// partial sums of all NT tokens are built in one pass over the row (each in
+// ascending i), then every step of the tree runs on all of them.
+template <typename XT, int HL, int NT>
+MOE_DEV void logits_group(const XT* xs, const float (&wf)[HL], int H, int t0, int l, float b, bool has_bias, int E,
+                          int e, float* __restrict__ logits) {
+    double p[NT];
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] = 0.0;
+#pragma unroll
+    for (int i = 0; i < HL; i++) {
+        const double wd = (double)wf[i];
+#pragma unroll
+        for (int k = 0; k < NT; k++) p[k] = __fma_rn(xval(xs + (long)(t0 + 2 * k) * H, l + i * WAVE), wd, p[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] += lane_down<32>(p[k]);
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] += lane_down<16>(p[k]);
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] += lane_down<8>(p[k]);
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] += lane_down<4>(p[k]);
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] += lane_down<2>(p[k]);
+#pragma unroll
+    for (int k = 0; k < NT; k++) p[k] += lane_down<1>(p[k]);
+    if (l == 0) {
+#pragma unroll
+        for (int k = 0; k < NT; k++) {
+            float v = (float)p[k];
+            if (has_bias) v = __fadd_rn(v, b);
+            logits[(long)(t0 + 2 * k) * E + e] = v;
+        }
+    }
+}
 
 template <typename XT, int HL>
-__global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict__ x, const float* __restrict__ wr,
+__global__ __launch_bounds__(256) void k_logits_exact_small(const XT* __restrict__ x, const float* __restrict__ wr,
                                                             const float* __restrict__ bias, int T, int H, int E,
                                                             float* __restrict__ logits) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     XT* xs = reinterpret_cast<XT*>(smem);
     const int tid = threadIdx.x;
     const int l = lane_id();
-    // the router row's loads go out first (a wave past E re-reads row E-1),
-    // then x [T][H] is staged with four 16-byte loads in flight per thread
-    const int e = blockIdx.x * 2 + tid / WAVE;
-    const int er = e < E ? e : E - 1;
+    const int wave = tid / WAVE;
+    const int e = blockIdx.x * 2 + (wave >> 1);
+    const int h = wave & 1;
+    const int er = e < E ? e : E - 1;              // a wave past E re-reads row E-1
+    // x [T][H] goes to LDS by the LDS DMA (1 KB of 16-byte chunks per wave
+    // instruction; the LDS is sized to whole 1 KB pieces and past the end the
+    // last chunk is loaded again into the padding), issued before the router
+    // row's loads so that it lands while the router row still streams in
+    const int per = 16 / (int)sizeof(XT);
+    const int nchunk = T * H / per;
+    const unsigned char* xg = reinterpret_cast<const unsigned char*>(x);
+    for (int c = wave * WAVE; c < nchunk; c += 4 * WAVE)
+        __builtin_amdgcn_global_load_lds(xg + (long)min(c + l, nchunk - 1) * 16, (lds_void_t*)(smem + (long)c * 16), 16,
+                                         0, 0);
     float wf[HL];
 #pragma unroll
     for (int i = 0; i < HL; i++) wf[i] = wr[(long)er * H + l + i * WAVE];   // H == 64 * HL
     const float b = bias ? bias[er] : 0.f;
-    // x [T][H] into LDS, 16 chunks of 16 bytes per thread in flight at a time
-    // (past the end the last chunk is loaded and stored again)
-    const int per = 16 / (int)sizeof(XT);
-    const int nchunk = T * H / per;
-    const uint4* xg = reinterpret_cast<const uint4*>(x);
-    uint4* xd = reinterpret_cast<uint4*>(xs);
-    for (int c0 = 0; c0 * 128 < nchunk; c0 += 16) {
-        uint4 a[16];
-#pragma unroll
-        for (int c = 0; c < 16; c++) a[c] = xg[min(tid + (c0 + c) * 128, nchunk - 1)];
-#pragma unroll
-        for (int c = 0; c < 16; c++) xd[min(tid + (c0 + c) * 128, nchunk - 1)] = a[c];
-    }
+    lm_wait_vmcnt<0>();
     __syncthreads();
     if (e >= E) return;
-    double w[HL];
-#pragma unroll
-    for (int i = 0; i < HL; i++) w[i] = (double)wf[i];
-    for (int t = 0; t < T; t++) {
-        double p = 0.0;
-#pragma unroll
-        for (int i = 0; i < HL; i++) p = __fma_rn(xval(xs + t * H, l + i * WAVE), w[i], p);
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) p += __shfl_xor(p, d, WAVE);
-        if (l == 0) {
-            float v = (float)p;
-            if (bias) v = __fadd_rn(v, b);
-            logits[(long)t * E + e] = v;
-        }
+    const int nt = (T - h + 1) / 2;                // tokens h, h + 2, ... below T
+    for (int k0 = 0; k0 < nt; k0 += XS_GROUP) {
+        const int t0 = h + 2 * k0;
+        const int m = nt - k0;
+        if (m >= 4) logits_group<XT, HL, 4>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        else if (m == 3) logits_group<XT, HL, 3>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        else if (m == 2) logits_group<XT, HL, 2>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        else logits_group<XT, HL, 1>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
     }
 }
 
@@ -618,12 +671,12 @@ __global__ __launch_bounds__(128) void k_logits_exact_small(const XT* __restrict
 template <int HL>
 static bool small_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
                         float* logits, hipStream_t st) {
-    const size_t lds = (size_t)T * H * (x_bf16 ? 2 : 4);
+    const size_t lds = ((size_t)T * H * (x_bf16 ? 2 : 4) + 1023) / 1024 * 1024;   // whole 1 KB DMA pieces
     if (x_bf16)
-        hipLaunchKernelGGL((k_logits_exact_small<uint16_t, HL>), dim3((E + 1) / 2), dim3(128), lds, st,
+        hipLaunchKernelGGL((k_logits_exact_small<uint16_t, HL>), dim3((E + 1) / 2), dim3(256), lds, st,
                            (const uint16_t*)x, wr, bias, T, H, E, logits);
     else
-        hipLaunchKernelGGL((k_logits_exact_small<float, HL>), dim3((E + 1) / 2), dim3(128), lds, st, (const float*)x,
+        hipLaunchKernelGGL((k_logits_exact_small<float, HL>), dim3((E + 1) / 2), dim3(256), lds, st, (const float*)x,
                            wr, bias, T, H, E, logits);
     return true;
 }
