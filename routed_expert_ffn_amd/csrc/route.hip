@@ -387,7 +387,10 @@ MOE_DEV void write_selection(float sel_v, int sel_i, int K, long t, int32_t* __r
     }
 }
 
-// One wave per token.  With exact logits the top K is final.  With estimates,
+// One wave per token; the leading values come from the threshold cut (the
+// K-th largest lane maximum bounds the candidates, which are then ranked),
+// with the round-by-round selection when more than 64 candidates pass it.
+// With exact logits the top K is final.  With estimates,
 // a token whose K+1 leading values are all separated by at least tau is final
 // too; any other token is queued, with its cut (K-th estimate - tau), for
 // k_route_recheck and written there.
@@ -434,7 +437,9 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     const int rounds = (exact || K == E) ? K : K + 1;
     uint32_t key;
     int sel_i;
-    select_top<VPL>(kv, rounds, key, sel_i);
+    __shared__ uint2 cut_scratch[4][2 * WAVE];
+    if (!select_top_cut<VPL>(kv, rounds, cut_scratch[wave], cut_scratch[wave] + WAVE, key, sel_i))
+        select_top<VPL>(kv, rounds, key, sel_i);
     const float sel_v = order_key_value(key);
     bool flagged = false;
     if (!exact) {
@@ -471,6 +476,7 @@ __global__ __launch_bounds__(1024) void k_route_select_group(const float* __rest
     int* cur = reinterpret_cast<int*>(mask + E);                              // [E]
     int* sidx = cur + E;                                                      // [T*K] selected experts
     __shared__ int wave_tot[16];
+    __shared__ uint2 cut_scratch[16][2 * WAVE];
     const int wave = threadIdx.x / WAVE, l = lane_id();
     for (int e = threadIdx.x; e < E; e += blockDim.x) { cur[e] = 0; mask[e] = 0ull; }
     if (wave < T) {
@@ -480,7 +486,8 @@ __global__ __launch_bounds__(1024) void k_route_select_group(const float* __rest
         load_order_keys<VPL>(row, E, kv);
         uint32_t key;
         int sel_i;
-        select_top<VPL>(kv, K, key, sel_i);
+        if (!select_top_cut<VPL>(kv, K, cut_scratch[wave], cut_scratch[wave] + WAVE, key, sel_i))
+            select_top<VPL>(kv, K, key, sel_i);
         write_selection(order_key_value(key), sel_i, K, t, idx_out, w_out);
         if (l < K) sidx[t * K + l] = sel_i;
     }
