@@ -51,12 +51,13 @@ struct VerifyOut {
 // gives them) by one wave, with the routing weights computed as moe_route
 // computes them; lane r < K ends with rank r's expert and weight.
 template <int VPL>
-MOE_DEV void select_weights(uint32_t (&kv)[VPL], int K, uint2* __restrict__ scratch, int& e_out, float& w_out) {
+MOE_DEV void select_weights(uint32_t (&kv)[VPL], int K, uint2* __restrict__ scratch, bool want_w, int& e_out,
+                            float& w_out) {
     uint32_t key;
     int sel;
     if (!select_top_cut<VPL>(kv, K, scratch, scratch + WAVE, key, sel)) select_top<VPL>(kv, K, key, sel);
     e_out = sel;
-    w_out = selection_weight(order_key_value(key), K);
+    w_out = want_w ? selection_weight(order_key_value(key), K) : 0.f;
 }
 
 // Calls f(u, v[u]) for u < n rounded up to 16, over an LDS array v of
@@ -82,31 +83,44 @@ MOE_DEV void for_slots(const int* __restrict__ v, int n, Fn&& f) {
 }
 
 // Routing and grouping of T <= 8 tokens inside one block of 8 waves (every
-// block of the gate/up launch runs it): wave t selects token t from the order
-// keys it loaded (kv, see the kernels); then the T*K slots are grouped by
-// expert, stable by slot: the grouped row of slot s is its rank in (expert,
-// slot) order, counted by the waves that hold slots only (one compare of
-// packed keys e * VMAX_SLOTS + s per slot).  Group starts over the sorted rows
-// become two 64-bit ballots, from which every touched expert's list index and
-// row count follow by population counts.  The writer block also stores the
-// routing and grouping outputs (counts and offsets by a binary search of each
-// expert in the touched list).  Needs T <= 8 and T*K <= VMAX_SLOTS <=
-// blockDim.x; returns the number of touched experts.  LDS: sel, srt
+// block of the gate/up launch runs it), in two phases so that the weight loads
+// of a wave's first items can go out between them.
+//
+// route_select_block: wave t selects token t from the order keys it loaded
+// (kv, see the kernels), stores the slot keys e * VMAX_SLOTS + s and sets the
+// selected experts' bits in `touched` (E bits, cleared beforehand; the j-th
+// touched expert in ascending order is touched_nth(j)).  The writer block also
+// stores ids and weights.
+//
+// route_group_rest: the T*K slots grouped by expert, stable by slot: the
+// grouped row of slot s is its rank in (expert, slot) order, counted by the
+// waves that hold slots only (one compare of packed keys per slot).  Group
+// starts over the sorted rows become two 64-bit ballots, from which every
+// touched expert's list index and row count follow by population counts.  The
+// writer block also stores the grouping outputs (counts and offsets by a
+// binary search of each expert in the touched list).  Returns the number of
+// touched experts.
+//
+// Needs T <= 8 and T*K <= VMAX_SLOTS <= blockDim.x.  LDS: sel, srt
 // [VMAX_SLOTS] int (16-byte aligned; slot keys, sorted keys); list [T*K] int4
 // (expert, first grouped row, rows), expert order; prow [T*K] int (token of
-// every grouped row); sscratch [8 waves][128] uint2 (the selection's scratch).
+// every grouped row); sscratch [8 waves][128] uint2 (the selection's scratch);
+// touched [VTOUCH_WORDS] uint64.
+constexpr int VTOUCH_WORDS = 16;     // E <= 1024
+
 template <int VPL>
-MOE_DEV int route_group_block(uint32_t (&kv)[VPL], int T, int E, int K, int* __restrict__ sel,
-                              int* __restrict__ srt, int4* __restrict__ list, int* __restrict__ prow,
-                              uint2* __restrict__ sscratch, bool writer, const VerifyOut& o) {
+MOE_DEV void route_select_block(uint32_t (&kv)[VPL], int T, int K, int* __restrict__ sel,
+                                uint64_t* __restrict__ touched, uint2* __restrict__ sscratch, bool writer,
+                                const VerifyOut& o) {
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
     const int n = T * K;
     if (wave < T) {
         int e;
         float w;
-        select_weights<VPL>(kv, K, sscratch + wave * 2 * WAVE, e, w);
+        select_weights<VPL>(kv, K, sscratch + wave * 2 * WAVE, writer, e, w);
         if (l < K) {
             sel[wave * K + l] = e * VMAX_SLOTS + wave * K + l;
+            __hip_atomic_fetch_or(touched + (e >> 6), 1ull << (e & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (writer) {
                 o.idx[wave * K + l] = e;
                 o.w[wave * K + l] = w;
@@ -115,6 +129,41 @@ MOE_DEV int route_group_block(uint32_t (&kv)[VPL], int T, int E, int K, int* __r
     }
     if (tid < VMAX_SLOTS - n) sel[n + tid] = 0x7fffffff;   // padding read by for_slots, never counted
     lds_barrier();
+}
+
+// Number of touched experts (wave-uniform).
+MOE_DEV int touched_count(const uint64_t* __restrict__ touched, int E) {
+    int c = 0;
+    for (int w = 0; w < (E + 63) / 64; w++) c += __popcll(touched[w]);
+    return c;
+}
+
+// The j-th touched expert in ascending order, j < touched_count (wave-uniform):
+// the word holding it by running population counts, then the bit whose count
+// of set bits below it is j's remainder (one ballot).
+MOE_DEV int touched_nth(const uint64_t* __restrict__ touched, int E, int j) {
+    int base = 0, wsel = 0, bsel = 0;
+    uint64_t msel = 0;
+    for (int w = 0; w < (E + 63) / 64; w++) {
+        const uint64_t m = touched[w];
+        const int c = __popcll(m);
+        if (j >= base && j < base + c) {
+            wsel = w;
+            msel = m;
+            bsel = base;
+        }
+        base += c;
+    }
+    const int l = lane_id();
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msel >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msel, 0));
+    const uint64_t b = __ballot(((msel >> l) & 1ull) && below == j - bsel);
+    return wsel * 64 + (__ffsll((long long)b) - 1);
+}
+
+MOE_DEV int route_group_rest(int T, int E, int K, const int* __restrict__ sel, int* __restrict__ srt,
+                             int4* __restrict__ list, int* __restrict__ prow, bool writer, const VerifyOut& o) {
+    const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    const int n = T * K;
     if (tid < n) {
         const int me = sel[tid];
         int pos = 0;
@@ -225,26 +274,29 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
     int* sel = reinterpret_cast<int*>(list + n);                      // [VMAX_SLOTS]
     int* srt = sel + VMAX_SLOTS;                                      // [VMAX_SLOTS]
     uint2* sscr = reinterpret_cast<uint2*>(srt + VMAX_SLOTS);       // [8][128]
-    int* prow = reinterpret_cast<int*>(sscr + 8 * 2 * WAVE);          // [n]
+    uint64_t* touched = reinterpret_cast<uint64_t*>(sscr + 8 * 2 * WAVE);   // [VTOUCH_WORDS]
+    int* prow = reinterpret_cast<int*>(touched + VTOUCH_WORDS);       // [n]
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    const bool writer = blockIdx.x == 0;
     // the token rows' loads go out first, then wave t's loads of token t's
     // logits; x goes to LDS while the selection waits for the logits
     XStage<NT, H, VG_THREADS> xst;
     xst.load_x(x, T);
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
+    if (tid < VTOUCH_WORDS) touched[tid] = 0ull;
     xst.store_x(xs, T);
-    const int nlist = route_group_block<VPL>(kv, T, E, K, sel, srt, list, prow, sscr, blockIdx.x == 0, o);
+    lds_barrier();
+    route_select_block<VPL>(kv, T, K, sel, touched, sscr, writer, o);
 
     const int tpe = F / FR;
-    const int n_items = nlist * tpe;
+    const int n_items = touched_count(touched, E) * tpe;
     const int W = gridDim.x * (VG_THREADS / WAVE);
     const int it = blockIdx.x * (VG_THREADS / WAVE) + wave;
     const bool active = it < n_items;
 
     uint4 wbuf[RING][2 * FR][CH];
-    auto load = [&](int item, uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
-        const int e = list[item / tpe].x, f0 = (item % tpe) * FR;
+    auto load_e = [&](int e, int f0, uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
         const uint16_t* g0 = wg + ((long)e * F + f0) * H + l * 8;
         const uint16_t* u0 = wu + ((long)e * F + f0) * H + l * 8;
 #pragma unroll
@@ -254,6 +306,9 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
                 w[r][c] = ldnt16(g0 + (long)r * H + c * 512);
                 w[FR + r][c] = ldnt16(u0 + (long)r * H + c * 512);
             }
+    };
+    auto load = [&](int item, uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
+        load_e(list[item / tpe].x, (item % tpe) * FR, w);
     };
     auto compute = [&](int item, const uint4 (&w)[2 * FR][CH]) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
@@ -285,8 +340,16 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
         };
         by_rows<NT>(nj, rows);
     };
-    if (active) ring_start<RING>(it, W, n_items, wbuf, load);
-    lds_barrier();
+    // the first items' weights (as ring_start would load them, their experts
+    // from the bitmap) go out before the grouping
+    if (active) {
+#pragma unroll
+        for (int b = 0; b < RING - 1; b++) {
+            const int item = min(it + b * W, n_items - 1);
+            load_e(touched_nth(touched, E, item / tpe), (item % tpe) * FR, wbuf[b]);
+        }
+    }
+    route_group_rest(T, E, K, sel, srt, list, prow, writer, o);
     if (!active) return;
     ring_run<RING>(it, W, n_items, wbuf, load, compute);
 }
@@ -307,19 +370,23 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
     int* sel = reinterpret_cast<int*>(list + n);                           // [VMAX_SLOTS]
     int* srt = sel + VMAX_SLOTS;                                           // [VMAX_SLOTS]
     uint2* sscr = reinterpret_cast<uint2*>(srt + VMAX_SLOTS);            // [8][128]
-    int* prow = reinterpret_cast<int*>(sscr + 8 * 2 * WAVE);               // [n]
+    uint64_t* touched = reinterpret_cast<uint64_t*>(sscr + 8 * 2 * WAVE);  // [VTOUCH_WORDS]
+    int* prow = reinterpret_cast<int*>(touched + VTOUCH_WORDS);            // [n]
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
+    const bool writer = blockIdx.x == 0;
     // the token rows' loads go out first, then wave t's loads of token t's
     // logits; x goes to LDS while the selection waits for the logits
     XStage<NT, H, VG_THREADS> xst;
     xst.load_x(x, T);
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
+    if (tid < VTOUCH_WORDS) touched[tid] = 0ull;
     xst.store_x(xs, T);
-    const int nlist = route_group_block<VPL>(kv, T, E, K, sel, srt, list, prow, sscr, blockIdx.x == 0, o);
+    lds_barrier();
+    route_select_block<VPL>(kv, T, K, sel, touched, sscr, writer, o);
 
     const int tpe = F / FR;
-    const int n_items = nlist * tpe;
+    const int n_items = touched_count(touched, E) * tpe;
     const int W = gridDim.x * (VG_THREADS / WAVE);
     const int it = blockIdx.x * (VG_THREADS / WAVE) + wave;
     const bool active = it < n_items;
@@ -327,8 +394,8 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
     constexpr int QW = QWords<QB>::n;
     struct Buf { uint32_t q[2 * FR][QW]; uint16_t d[2 * FR]; };
     Buf wbuf[RING];
-    auto load = [&](int item, Buf& b) __attribute__((always_inline)) {
-        const long row0 = (long)list[item / tpe].x * F + (item % tpe) * FR;
+    auto load_e = [&](int e, int f0, Buf& b) __attribute__((always_inline)) {
+        const long row0 = (long)e * F + f0;
 #pragma unroll
         for (int r = 0; r < FR; r++) {
             load_block<QB>(b.q[r], wg + (row0 + r) * (H * QB / 8), H, l);
@@ -336,6 +403,9 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
             b.d[r] = ldnt_u16(sg + (row0 + r) * (H / 32) + l);
             b.d[FR + r] = ldnt_u16(su + (row0 + r) * (H / 32) + l);
         }
+    };
+    auto load = [&](int item, Buf& b) __attribute__((always_inline)) {
+        load_e(list[item / tpe].x, (item % tpe) * FR, b);
     };
     auto compute = [&](int item, const Buf& b) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
@@ -368,8 +438,16 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
         };
         by_rows<NT>(nj, rows);
     };
-    if (active) ring_start<RING>(it, W, n_items, wbuf, load);
-    lds_barrier();
+    // the first items' weights (as ring_start would load them, their experts
+    // from the bitmap) go out before the grouping
+    if (active) {
+#pragma unroll
+        for (int b = 0; b < RING - 1; b++) {
+            const int item = min(it + b * W, n_items - 1);
+            load_e(touched_nth(touched, E, item / tpe), (item % tpe) * FR, wbuf[b]);
+        }
+    }
+    route_group_rest(T, E, K, sel, srt, list, prow, writer, o);
     block_sums(xs, T, H, xsum);
     lds_barrier();
     if (!active) return;
@@ -636,7 +714,7 @@ constexpr int VDQ_RING = 8;                // quantised down
 size_t gateup_lds(int T, int K, int quant) {
     const size_t n = (size_t)T * K;
     return (size_t)T * VH * 2 + (quant ? (size_t)T * (VH / 32) * 4 : 0) + n * 16 + 2 * VMAX_SLOTS * 4 +
-           8 * 2 * WAVE * 8 + n * 4;
+           8 * 2 * WAVE * 8 + VTOUCH_WORDS * 8 + n * 4;
 }
 size_t down_lds(int T, int K, int quant) {
     const size_t n = (size_t)T * K;
