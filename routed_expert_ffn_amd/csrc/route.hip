@@ -567,10 +567,11 @@ __global__ __launch_bounds__(256) void k_route_recheck(const float* __restrict__
 
 // ------------------------------------------------------------------ exact logits, few tokens
 
-// Two waves per expert, each taking every other token (h, h + 2, ...): the
-// router row (H fp32) is held in registers (H/64 independent loads per lane in
-// flight), the token rows are staged in LDS.  Two experts per block, so a
-// block's four waves fill a CU's four SIMDs.
+// G = 2 or 4 waves per expert, wave h taking tokens h, h + G, ...: the router
+// row (H fp32) is held in registers (H/64 independent loads per lane in
+// flight), the token rows are staged in LDS.  4 / G experts per block, so a
+// block's four waves fill a CU's four SIMDs; G = 4 when two experts per block
+// would leave CUs without a block.
 constexpr int XS_MAX_T = 16;
 constexpr int XS_GROUP = 4;          // tokens whose partial sums a wave builds together
 
@@ -596,10 +597,10 @@ MOE_DEV double lane_down(double v) {
     return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// Logits of NT tokens t0, t0 + 2, ... for this wave's expert: the strided
+// Logits of NT tokens t0, t0 + G, ... for this wave's expert: the strided
 // partial sums of all NT tokens are built in one pass over the row (each in
 // ascending i), then every step of the tree runs on all of them.
-template <typename XT, int HL, int NT>
+template <typename XT, int HL, int NT, int G>
 MOE_DEV void logits_group(const XT* xs, const float (&wf)[HL], int H, int t0, int l, float b, bool has_bias, int E,
                           int e, float* __restrict__ logits) {
     double p[NT];
@@ -609,7 +610,7 @@ MOE_DEV void logits_group(const XT* xs, const float (&wf)[HL], int H, int t0, in
     for (int i = 0; i < HL; i++) {
         const double wd = (double)wf[i];
 #pragma unroll
-        for (int k = 0; k < NT; k++) p[k] = __fma_rn(xval(xs + (long)(t0 + 2 * k) * H, l + i * WAVE), wd, p[k]);
+        for (int k = 0; k < NT; k++) p[k] = __fma_rn(xval(xs + (long)(t0 + G * k) * H, l + i * WAVE), wd, p[k]);
     }
 #pragma unroll
     for (int k = 0; k < NT; k++) p[k] += lane_down<32>(p[k]);
@@ -628,12 +629,12 @@ MOE_DEV void logits_group(const XT* xs, const float (&wf)[HL], int H, int t0, in
         for (int k = 0; k < NT; k++) {
             float v = (float)p[k];
             if (has_bias) v = __fadd_rn(v, b);
-            logits[(long)(t0 + 2 * k) * E + e] = v;
+            logits[(long)(t0 + G * k) * E + e] = v;
         }
     }
 }
 
-template <typename XT, int HL>
+template <typename XT, int HL, int G>
 __global__ __launch_bounds__(256) void k_logits_exact_small(const XT* __restrict__ x, const float* __restrict__ wr,
                                                             const float* __restrict__ bias, int T, int H, int E,
                                                             float* __restrict__ logits) {
@@ -642,8 +643,8 @@ __global__ __launch_bounds__(256) void k_logits_exact_small(const XT* __restrict
     const int tid = threadIdx.x;
     const int l = lane_id();
     const int wave = tid / WAVE;
-    const int e = blockIdx.x * 2 + (wave >> 1);
-    const int h = wave & 1;
+    const int e = blockIdx.x * (4 / G) + wave / G;
+    const int h = wave % G;
     const int er = e < E ? e : E - 1;              // a wave past E re-reads row E-1
     // x [T][H] goes to LDS by the LDS DMA (1 KB of 16-byte chunks per wave
     // instruction; the LDS is sized to whole 1 KB pieces and past the end the
@@ -662,29 +663,38 @@ __global__ __launch_bounds__(256) void k_logits_exact_small(const XT* __restrict
     lm_wait_vmcnt<0>();
     __syncthreads();
     if (e >= E) return;
-    const int nt = (T - h + 1) / 2;                // tokens h, h + 2, ... below T
+    const int nt = (T - h + G - 1) / G;            // tokens h, h + G, ... below T
     for (int k0 = 0; k0 < nt; k0 += XS_GROUP) {
-        const int t0 = h + 2 * k0;
+        const int t0 = h + G * k0;
         const int m = nt - k0;
-        if (m >= 4) logits_group<XT, HL, 4>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
-        else if (m == 3) logits_group<XT, HL, 3>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
-        else if (m == 2) logits_group<XT, HL, 2>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
-        else logits_group<XT, HL, 1>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        if (m >= 4) logits_group<XT, HL, 4, G>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        else if (m == 3) logits_group<XT, HL, 3, G>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        else if (m == 2) logits_group<XT, HL, 2, G>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
+        else logits_group<XT, HL, 1, G>(xs, wf, H, t0, l, b, bias != nullptr, E, e, logits);
     }
 }
 
 // ------------------------------------------------------------------ launchers
 
+template <int HL, int G>
+static void small_exact_g(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
+                          float* logits, hipStream_t st) {
+    const size_t lds = ((size_t)T * H * (x_bf16 ? 2 : 4) + 1023) / 1024 * 1024;   // whole 1 KB DMA pieces
+    const dim3 grid((E + 4 / G - 1) / (4 / G));
+    if (x_bf16)
+        hipLaunchKernelGGL((k_logits_exact_small<uint16_t, HL, G>), grid, dim3(256), lds, st, (const uint16_t*)x, wr,
+                           bias, T, H, E, logits);
+    else
+        hipLaunchKernelGGL((k_logits_exact_small<float, HL, G>), grid, dim3(256), lds, st, (const float*)x, wr, bias,
+                           T, H, E, logits);
+}
 template <int HL>
 static bool small_exact(const void* x, int x_bf16, const float* wr, const float* bias, int T, int H, int E,
                         float* logits, hipStream_t st) {
-    const size_t lds = ((size_t)T * H * (x_bf16 ? 2 : 4) + 1023) / 1024 * 1024;   // whole 1 KB DMA pieces
-    if (x_bf16)
-        hipLaunchKernelGGL((k_logits_exact_small<uint16_t, HL>), dim3((E + 1) / 2), dim3(256), lds, st,
-                           (const uint16_t*)x, wr, bias, T, H, E, logits);
-    else
-        hipLaunchKernelGGL((k_logits_exact_small<float, HL>), dim3((E + 1) / 2), dim3(256), lds, st, (const float*)x,
-                           wr, bias, T, H, E, logits);
+    int ncu = 0;
+    if (current_device_cus(&ncu) != hipSuccess || ncu <= 0) ncu = 256;
+    if ((E + 1) / 2 < ncu) small_exact_g<HL, 4>(x, x_bf16, wr, bias, T, H, E, logits, st);
+    else small_exact_g<HL, 2>(x, x_bf16, wr, bias, T, H, E, logits, st);
     return true;
 }
 
