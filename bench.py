@@ -195,10 +195,21 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
     acct = layer_bytes_and_flops(shape, counts, synth.expert_bytes(shape))
 
     fns = [(capture(torch, lambda L=L: step(L)).replay if use_graph else (lambda L=L: step(L))) for L in layers]
+    # consecutive steps run as one graph of the `sets` layer calls in rotation
+    # order (as a model's consecutive layers would), so that a step does not
+    # carry a whole graph launch; a partial rotation replays single-call graphs
+    run_all = capture(torch, lambda: [step(L) for L in layers]).replay if use_graph and sets > 1 else None
 
     def run_steps(n, start):
-        for i in range(n):
-            fns[(start + i) % sets]()
+        i = 0
+        while i < n:
+            j = (start + i) % sets
+            if run_all is not None and j == 0 and n - i >= sets:
+                run_all()
+                i += sets
+            else:
+                fns[j]()
+                i += 1
 
     timer = Timer(torch)
     if warmup > 0:
@@ -211,7 +222,8 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
     f_all = acct[0]["f_ffn"] + acct[0]["f_router"]
     touched = sum(a["touched"] for a in acct) / len(acct)
     res = dict(name=name, T=shape.T, ms_per_step=ms, value=shape.T / (ms / 1e3), steps=steps, warmup=warmup,
-               wall_s=wall, step_us=stats, touched_experts=touched, bytes_per_step=b_step,
+               wall_s=wall, step_us=stats, layers_per_graph=sets if run_all is not None else 1,
+               touched_experts=touched, bytes_per_step=b_step,
                bytes_experts=sum(a["b_experts"] for a in acct) / len(acct), flops_ffn=f_ffn, flops_step=f_all,
                hbm_frac_step=b_step / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
                mfma_frac_step=f_all / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
@@ -657,7 +669,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": main_res["name"], "tokens": main_res.get("T"), "hidden": 2048, "experts": 512,
                    "top_k": 10, "expert_width": 512, "weight_sets_rotated": N_SETS if is_verify else 1,
-                   "hip_graph": use_graph},
+                   "hip_graph": use_graph, "layer_calls_per_graph": main_res.get("layers_per_graph", 1)},
         "roofline": main_res.get("roofline"),
         "cpu_baseline": main_res.get("cpu_baseline"),
         "step_us": main_res.get("step_us"),
