@@ -197,6 +197,45 @@ def test_layer_few_tokens_fused_many_experts_and_ties():
     assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
 
 
+def test_layer_few_tokens_fused_max_experts():
+    """The fused path at its largest expert count (1024: 16 logits per lane,
+    a 16-word touched-expert bitmap), checked against the oracle on host
+    copies of the touched experts only (the other experts' weights are zero
+    pages the oracle never reads)."""
+    s = synth.LayerShape(T=8, H=2048, E=1024, K=10, F=512, act="bf16", wdt="bf16")
+    d = synth.make_device_layer(s, seed=4, cfg=9, layer=0, device="cuda")
+    torch.cuda.synchronize()
+    x, wr = to_host(d.x), to_host(d.wr)
+    ref_idx, ref_w, _ = oracle.route(x, wr, s.K)
+    out, r = run_layer(d)
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    wg = np.zeros((s.E, s.F, s.H), np.uint16)
+    wu = np.zeros((s.E, s.F, s.H), np.uint16)
+    wd = np.zeros((s.E, s.H, s.F), np.uint16)
+    for e in np.unique(ref_idx):
+        wg[e], wu[e], wd[e] = to_host(d.wg[e]), to_host(d.wu[e]), to_host(d.wd[e])
+    ref_out = oracle.layer_rows(x, ref_idx, ref_w, oracle.Weights("bf16", wg, wu, wd))
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
+@pytest.mark.parametrize("T,E,H,act", [(16, 520, 2048, "bf16"), (13, 513, 1024, "f32"), (5, 257, 512, "bf16"),
+                                       (2, 1024, 256, "f32"), (1, 512, 2048, "bf16")])
+def test_exact_logits_few_tokens_wave_splits(T, E, H, act):
+    """The few-token exact logits where an expert's tokens are split over two
+    waves (two experts per block; an odd expert count leaves the last block
+    half empty) or four, with up to two groups of four tokens per wave:
+    bit-exact against the oracle's pinned summation, same selection."""
+    s = synth.LayerShape(T=T, H=H, E=E, K=8, F=8, act=act, wdt="bf16", zipf=True)
+    h = synth.make_host_layer(s, seed=T + E, cfg=9)
+    d = device_from_host(h)
+    ref_idx, _, ref_lg = oracle.route(h.x, h.wr, s.K, h.bias)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx, _ = moe.route(d.x, d.wr, s.K, bias=d.bias, logits_out=lg)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(lg).view(np.uint32), ref_lg.view(np.uint32)), "logits are not bit-exact"
+    assert np.array_equal(to_host(idx), ref_idx)
+
+
 @pytest.mark.parametrize("wdt", ["bf16", "int4"])
 @pytest.mark.parametrize("T", [8, 9, 16, 17, 63, 65])
 def test_path_boundaries(T, wdt):
