@@ -20,50 +20,64 @@ MOE_DEV void combine_acc8(const void* __restrict__ y, const int32_t* __restrict_
                           const void* __restrict__ res, int t, int h, int K, int H, float (&acc)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = 0.f;
-    // K routed rows in groups of KB: the group's row loads are all in flight
-    // before its multiply-adds, which run in k order
-    constexpr int KB = 8;
-    for (int k0 = 0; k0 < K; k0 += KB) {
-        float v[KB][8];
-        float wk[KB];
-#pragma unroll
-        for (int u = 0; u < KB; u++) {
-            const int k = min(k0 + u, K - 1);          // past K: re-read the last row (unused)
-            const long row = inv[(long)t * K + k];
-            wk[u] = w[(long)t * K + k];
-            if constexpr (YB) {
-                const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)y + row * H + h);
-                const uint32_t uu[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int i = 0; i < 4; i++) { v[u][2 * i] = bf16lo_to_f32(uu[i]); v[u][2 * i + 1] = bf16hi_to_f32(uu[i]); }
-            } else {
-                const float4 a = *reinterpret_cast<const float4*>((const float*)y + row * H + h);
-                const float4 b = *reinterpret_cast<const float4*>((const float*)y + row * H + h + 4);
-                v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
-                v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < KB; u++) {
-            if (k0 + u < K) {                           // uniform
-#pragma unroll
-                for (int i = 0; i < 8; i++) acc[i] = fmaf(wk[u], v[u][i], acc[i]);
-            }
-        }
-    }
     const long o = (long)t * H + h;
-    if (res) {
+    // the residual chunk's load goes out with the first group's row loads
+    float rv[8];
+    auto load_res = [&]() __attribute__((always_inline)) {
         if constexpr (OB) {
             const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)res + o);
             const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int i = 0; i < 4; i++) { acc[2 * i] += bf16lo_to_f32(u[i]); acc[2 * i + 1] += bf16hi_to_f32(u[i]); }
+            for (int i = 0; i < 4; i++) { rv[2 * i] = bf16lo_to_f32(u[i]); rv[2 * i + 1] = bf16hi_to_f32(u[i]); }
         } else {
             const float4 a = *reinterpret_cast<const float4*>((const float*)res + o);
             const float4 b = *reinterpret_cast<const float4*>((const float*)res + o + 4);
-            acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-            acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+            rv[0] = a.x; rv[1] = a.y; rv[2] = a.z; rv[3] = a.w;
+            rv[4] = b.x; rv[5] = b.y; rv[6] = b.z; rv[7] = b.w;
         }
+    };
+    // K routed rows in groups of KB (K <= KB: one group): the group's row
+    // loads are all in flight before its multiply-adds, which run in k order
+    constexpr int KB = 16;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        uint4 q[KB][YB ? 1 : 2];                        // the rows as loaded, widened at their multiply-adds
+        float wk[KB];
+#pragma unroll
+        for (int u = 0; u < KB; u++) {
+            if (k0 + u < K) {                           // uniform
+                const long row = inv[(long)t * K + k0 + u];
+                wk[u] = w[(long)t * K + k0 + u];
+                if constexpr (YB) {
+                    q[u][0] = *reinterpret_cast<const uint4*>((const uint16_t*)y + row * H + h);
+                } else {
+                    q[u][0] = *reinterpret_cast<const uint4*>((const float*)y + row * H + h);
+                    q[u][YB ? 0 : 1] = *reinterpret_cast<const uint4*>((const float*)y + row * H + h + 4);
+                }
+            }
+        }
+        if (k0 == 0 && res) load_res();
+#pragma unroll
+        for (int u = 0; u < KB; u++) {
+            if (k0 + u < K) {                           // uniform
+                float v[8];
+                if constexpr (YB) {
+                    const uint32_t uu[4] = {q[u][0].x, q[u][0].y, q[u][0].z, q[u][0].w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) { v[2 * i] = bf16lo_to_f32(uu[i]); v[2 * i + 1] = bf16hi_to_f32(uu[i]); }
+                } else {
+                    const uint4 a = q[u][0], b = q[u][YB ? 0 : 1];
+                    const uint32_t uu[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int i = 0; i < 8; i++) v[i] = __uint_as_float(uu[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; i++) acc[i] = fmaf(wk[u], v[i], acc[i]);
+            }
+        }
+    }
+    if (res) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] += rv[i];
     }
 }
 
