@@ -83,7 +83,9 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ chunk_
     if (threadIdx.x == 0) offsets[E] = total;
 }
 
-// Pass 3: stable scatter, one wave per chunk.
+// Pass 3: stable scatter, one wave per chunk.  The chunk's expert ids (16
+// per lane) and the cursor inputs (8 experts per lane at a time) are loaded
+// with all their loads in flight before the scatter's sequential steps.
 __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ idx, int n, int E,
                                                      const int32_t* __restrict__ chunk_base,
                                                      const int32_t* __restrict__ offsets,
@@ -91,13 +93,35 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
     int* cur = reinterpret_cast<int*>(mask + E);
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        cur[e] = offsets[e] + chunk_base[(long)blockIdx.x * E + e];
-        mask[e] = 0ull;
+    const int l = threadIdx.x;
+    constexpr int G = PERM_CHUNK / WAVE;
+    const int s0 = blockIdx.x * PERM_CHUNK, s1 = min(n, s0 + PERM_CHUNK);
+    int ev[G];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const int s = s0 + g * WAVE + l;
+        ev[g] = s < s1 ? idx[s] : -1;
+    }
+    const int32_t* cb = chunk_base + (long)blockIdx.x * E;
+    for (int e0 = 0; e0 < E; e0 += 8 * WAVE) {
+        int a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int e = e0 + u * WAVE + l;
+            a[u] = e < E ? offsets[e] : 0;
+            b[u] = e < E ? cb[e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int e = e0 + u * WAVE + l;
+            if (e < E) {
+                cur[e] = a[u] + b[u];
+                mask[e] = 0ull;
+            }
+        }
     }
     __syncthreads();
-    const int s0 = blockIdx.x * PERM_CHUNK, s1 = min(n, s0 + PERM_CHUNK);
-    wave_stable_scatter(idx, s0, s1, E, cur, mask, perm, inv);
+    wave_stable_scatter_regs<G>(ev, s0, s1, E, cur, mask, perm, inv);
 }
 
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
