@@ -222,11 +222,80 @@ MOE_DEV float dot_block_low(const uint32_t (&q)[QB], const uint16_t* __restrict_
     }
     return d;
 }
+// Pair order: the same blocks decoded with one v_and_or per bf16 pair.  Masking
+// a packed word, shifted by s, with 0x000F000F (int4) or 0x00030003 (int2)
+// leaves one level in each 16-bit half, and or-ing 0x4300 into both halves
+// makes the pair 128 + u directly (no byte permute).  The two levels of a pair
+// lie 4 elements apart (int4: e_i, e_{i+4} of every 8; int2: e_{4k}, e_{4k+2}
+// and e_{4k+1}, e_{4k+3}), so the activations are kept in LDS in that pair
+// order (pair_order below, applied as they are staged): each dword of an
+// 8-element chunk holds the two activations of one weight pair.  The products
+// and the block sums are the same; only which products share a dot2 differs.
+template <int QB>
+MOE_DEV uint4 pair_order(uint4 v) {
+    if constexpr (QB == 4) {
+        return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                          __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+    } else if constexpr (QB == 2) {
+        return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                          __builtin_amdgcn_perm(v.w, v.z, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+    } else {
+        return v;   // int3 and bf16 rows keep the natural order
+    }
+}
+// 0x43004300 in a VGPR that the compiler cannot see through: with the or
+// constant in a register, (w & mask) | c becomes one v_and_or_b32 (the mask
+// from an SGPR; one instruction may read only one scalar operand); with two
+// constants it would take an and and an or.
+MOE_DEV uint32_t exp_pair() {
+    uint32_t c;
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(c));
+    return c;
+}
+MOE_DEV uint32_t lev_pair(uint32_t w, uint32_t mask, uint32_t c) { return (w & mask) | c; }
+MOE_DEV float dot_block_q4p(uint4 q, const uint16_t* __restrict__ xl) {
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t c = exp_pair();
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {   // elements 8k .. 8k+7
+        const uint4 xv = *reinterpret_cast<const uint4*>(xl + k * 8);
+        const uint32_t w = w4[k];
+        d = dot2bf(lev_pair(w, 0x000F000Fu, c), xv.x, d);
+        d = dot2bf(lev_pair(w >> 4, 0x000F000Fu, c), xv.y, d);
+        d = dot2bf(lev_pair(w >> 8, 0x000F000Fu, c), xv.z, d);
+        d = dot2bf(lev_pair(w >> 12, 0x000F000Fu, c), xv.w, d);
+    }
+    return d;
+}
+MOE_DEV float dot_block_q2p(const uint32_t (&q)[2], const uint16_t* __restrict__ xl) {
+    const uint32_t c = exp_pair();
+    float d = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; g++) {   // elements 16g .. 16g+15; element 4k + j in byte j, bits 2k, 2k+1
+        const uint4 xa = *reinterpret_cast<const uint4*>(xl + g * 16);
+        const uint4 xb = *reinterpret_cast<const uint4*>(xl + g * 16 + 8);
+        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            d = dot2bf(lev_pair(q[g] >> (2 * k), 0x00030003u, c), xw[2 * k], d);
+            d = dot2bf(lev_pair(q[g] >> (2 * k + 8), 0x00030003u, c), xw[2 * k + 1], d);
+        }
+    }
+    return d;
+}
 // one lane's block: 4 dwords (int4), 2 (int2) or 3 (int3)
 template <int QB> struct QWords { static constexpr int n = QB == 4 ? 4 : QB; };
 template <int QB>
 MOE_DEV float dot_block(const uint32_t (&q)[QWords<QB>::n], const uint16_t* __restrict__ xl) {
     if constexpr (QB == 4) return dot_block_q4(make_uint4(q[0], q[1], q[2], q[3]), xl);
+    else return dot_block_low<QB>(q, xl);
+}
+// the same with the activations in pair order (pair_order<QB>)
+template <int QB>
+MOE_DEV float dot_block_p(const uint32_t (&q)[QWords<QB>::n], const uint16_t* __restrict__ xl) {
+    if constexpr (QB == 4) return dot_block_q4p(make_uint4(q[0], q[1], q[2], q[3]), xl);
+    else if constexpr (QB == 2) return dot_block_q2p(q, xl);
     else return dot_block_low<QB>(q, xl);
 }
 // the lane's block of a row of n inputs at `row` (bytes n*QB/8), block b

@@ -229,11 +229,13 @@ struct XStage {
 #pragma unroll
         for (int c = 0; c < MAXC; c++) r[c] = g[min((int)threadIdx.x + c * THREADS, n16 - 1)];
     }
+    // QB: the rows go to LDS in the pair order of QB-bit weights (pair_order)
+    template <int QB>
     MOE_DEV void store_x(uint16_t* __restrict__ xs, int T) {
         const int n16 = T * H * 2 / 16;
 #pragma unroll
         for (int c = 0; c < MAXC; c++)   // past the end: the last chunk again, same value
-            reinterpret_cast<uint4*>(xs)[min((int)threadIdx.x + c * THREADS, n16 - 1)] = r[c];
+            reinterpret_cast<uint4*>(xs)[min((int)threadIdx.x + c * THREADS, n16 - 1)] = pair_order<QB>(r[c]);
     }
 };
 
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
     if (tid < VTOUCH_WORDS) touched[tid] = 0ull;
-    xst.store_x(xs, T);
+    xst.template store_x<16>(xs, T);
     lds_barrier();
     route_select_block<VPL>(kv, T, K, sel, touched, sscr, writer, o);
 
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
     if (tid < VTOUCH_WORDS) touched[tid] = 0ull;
-    xst.store_x(xs, T);
+    xst.template store_x<QB>(xs, T);
     lds_barrier();
     route_select_block<VPL>(kv, T, K, sel, touched, sscr, writer, o);
 
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
                     const float S = xsum[tok * (H / 32) + l];
 #pragma unroll
                     for (int r = 0; r < 2 * FR; r++) {
-                        const float D = dot_block<QB>(b.q[r], xl);
+                        const float D = dot_block_p<QB>(b.q[r], xl);
                         acc[r * NTN + t] = fmaf(fp16_to_f32(b.d[r]), fmaf(-zero_level<QB>(), S, D), acc[r * NTN + t]);
                     }
                 }
@@ -507,11 +509,12 @@ struct DownStage {
         w = topk_w[min(tid, n - 1)];
         p = inv[min(tid, n - 1)];
     }
+    template <int QB>   // the rows in the pair order of QB-bit weights (pair_order)
     MOE_DEV void store(uint16_t* __restrict__ as, float* __restrict__ tw, int* __restrict__ tinv, int n) const {
         const int n16 = n * VF * 2 / 16, tid = threadIdx.x;
         uint4* d = reinterpret_cast<uint4*>(as);
 #pragma unroll
-        for (int i = 0; i < MS; i++) d[min(tid + i * 512, n16 - 1)] = c[i];
+        for (int i = 0; i < MS; i++) d[min(tid + i * 512, n16 - 1)] = pair_order<QB>(c[i]);
         if (tid < n) {
             tw[tid] = w;
             tinv[tid] = p;
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(512) void k_vdown(const uint16_t* __restrict__ abuf
     };
     uint4 w0[VB], w1[VB];
     load(0, w0);
-    stg.store(as, tw, tinv, n);
+    stg.template store<16>(as, tw, tinv, n);
     lds_barrier();
     for (int jb = 0; jb < nlist; jb += 2 * VB) {
         load(jb + VB, w1);
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(512) void k_vdown_q(const uint16_t* __restrict__ ab
                 acc[t] = 0.f;
                 if (t < nj) {
                     const float S = asum[(off + t) * NB + b];
-                    const float D = dot_block<QB>(bf.q, as + (off + t) * F + b * 32);
+                    const float D = dot_block_p<QB>(bf.q, as + (off + t) * F + b * 32);
                     acc[t] = d * fmaf(-zero_level<QB>(), S, D);
                 }
             }
@@ -673,7 +676,7 @@ __global__ __launch_bounds__(512) void k_vdown_q(const uint16_t* __restrict__ ab
         by_rows<NT>(nj, rows);
     };
     if (n_items > 0) ring_start<RING>(0, 1, n_items, wb, load);
-    stg.store(as, tw, tinv, n);
+    stg.template store<QB>(as, tw, tinv, n);
     lds_barrier();
     block_sums(as, n, F, asum);
     lds_barrier();
