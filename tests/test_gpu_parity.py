@@ -181,6 +181,24 @@ def test_layer_few_tokens_fused(T, E, K, wdt, zipf, with_res, steer):
     assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
 
 
+@pytest.mark.parametrize("wdt", ["int4", "int3", "int2"])
+def test_layer_few_tokens_fused_lowbit_eighty_slots(wdt):
+    """moe_layer with block-quantised experts at T = 8, K = 10 (80 slots: the
+    down launch stages more than 64 grouped rows, and the int4 / int2 levels
+    are decoded in pair order against activations staged in that order, some
+    experts holding several rows): routing exact, outputs within the bf16
+    bound of the oracle.  (moe_ffn's separate low-bit path stops at 59 slots.)"""
+    s = synth.LayerShape(T=8, H=2048, E=48, K=10, F=512, act="bf16", wdt=wdt, zipf=True)
+    h = synth.make_host_layer(s, seed=80, cfg=9)
+    d = device_from_host(h)
+    ref_idx, ref_w, _ = oracle.route(h.x, h.wr, s.K, h.bias)
+    out, r = run_layer(d, residual=d.x)
+    check_routing_and_grouping(r, ref_idx, ref_w, s.E)
+    assert int(to_host(r["counts"]).max()) >= 4, "want experts with several rows"
+    ref_out = oracle.layer_rows(h.x, ref_idx, ref_w, host_weights(d), residual=h.x)
+    assert row_rel_err(to_host(out), ref_out) <= TOL_BF16
+
+
 def test_layer_few_tokens_fused_many_experts_and_ties():
     """The fused path's selection over more than 512 experts (16 logits per
     lane), with exact logit ties (duplicated router rows: the lower id wins)."""
