@@ -244,9 +244,11 @@ MOE_DEV uint4 pair_order(uint4 v) {
     }
 }
 // 0x43004300 in a VGPR that the compiler cannot see through: with the or
-// constant in a register, (w & mask) | c becomes one v_and_or_b32 (the mask
-// from an SGPR; one instruction may read only one scalar operand); with two
-// constants it would take an and and an or.
+// constant in a register, (w & mask) | c can be one v_and_or_b32 (the mask
+// from an SGPR; one instruction may read only one scalar operand), where with
+// two constants it is always an and and an or.  Where the weights serve
+// several token rows the compiler still hoists the and out of the per-row
+// code and keeps a separate or per row.
 MOE_DEV uint32_t exp_pair() {
     uint32_t c;
     asm("v_mov_b32 %0, 0x43004300" : "=v"(c));
