@@ -257,6 +257,7 @@ MOE_DEV void copy_to_lds(const void* __restrict__ src, void* __restrict__ dst, i
 }
 
 constexpr int VG_THREADS = 512;   // gate/up blocks: 8 waves, one token's selection each
+constexpr int VQ_ROWS = 2;        // token rows per pass of the quantised gate/up
 
 }  // namespace
 
@@ -412,16 +413,18 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
     auto compute = [&](int item, const Buf& b) __attribute__((always_inline)) {
         const int4 ent = list[item / tpe];
         const int off = ent.y, nj = __builtin_amdgcn_readfirstlane(ent.z), f0 = (item % tpe) * FR;
-        auto rows = [&](auto ntn) __attribute__((always_inline)) {
+        // rows t0 .. t0 + NTN - 1 of the item's expert
+        auto rows = [&](auto ntn, int t0) __attribute__((always_inline)) {
             constexpr int NTN = decltype(ntn)::value;
             constexpr int V = 2 * FR * NTN;
+            const int nr = nj - t0;
             float acc[V];
 #pragma unroll
             for (int i = 0; i < V; i++) acc[i] = 0.f;
 #pragma unroll
             for (int t = 0; t < NTN; t++) {
-                if (t < nj) {
-                    const int tok = prow[off + t];
+                if (t < nr) {
+                    const int tok = prow[off + t0 + t];
                     const uint16_t* xl = xs + tok * H + l * 32;
                     const float S = xsum[tok * (H / 32) + l];
 #pragma unroll
@@ -435,10 +438,16 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup_q(
             constexpr int shift = tr_shift<V>();
             const float up = __shfl_down(v, (FR * NTN) << shift, WAVE);
             const int j = l >> shift, r = j / NTN, t = j % NTN;
-            if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < nj)
-                abuf[(long)(off + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
+            if ((l & ((1 << shift) - 1)) == 0 && r < FR && t < nr)
+                abuf[(long)(off + t0 + t) * F + f0 + r] = f32_to_bf16_rne(silu_ref(v) * up);
         };
-        by_rows<NT>(nj, rows);
+        // at most VQ_ROWS rows per pass (more rows: further passes over the
+        // same weights), which bounds the accumulators and the reduction
+        if (nj <= VQ_ROWS) {
+            by_rows<(NT < VQ_ROWS ? NT : VQ_ROWS)>(nj, [&](auto ntn) __attribute__((always_inline)) { rows(ntn, 0); });
+        } else {
+            for (int t0 = 0; t0 < nj; t0 += VQ_ROWS) rows(std::integral_constant<int, VQ_ROWS>{}, t0);
+        }
     };
     // the first items' weights (as ring_start would load them, their experts
     // from the bitmap) go out before the grouping
