@@ -14,7 +14,7 @@
 //      outputs and the touched-expert list.  Then the gate/up weight stream of
 //      the touched experts (as in ffn_stream.hip) writes a = bf16(silu(g) u);
 //   3. k_vdown / k_vdown_q: one wave per hidden row (bf16) or per four rows
-//      and a quarter of the touched experts (block-quantised weights) walks the
+//      and an eighth of the touched experts (block-quantised weights) walks the
 //      touched experts' down rows, keeps each grouped row's output in LDS and
 //      then combines each token's K outputs in k order with the residual, one
 //      rounding: y_perm never goes to memory and no combine launch runs.
@@ -257,7 +257,7 @@ MOE_DEV void copy_to_lds(const void* __restrict__ src, void* __restrict__ dst, i
 }
 
 constexpr int VG_THREADS = 512;   // gate/up blocks: 8 waves, one token's selection each
-constexpr int VQ_ROWS = 2;        // token rows per pass of the quantised gate/up
+constexpr int VQ_ROWS = 2;        // token rows per pass of the quantised gate/up and down
 
 }  // namespace
 
@@ -500,11 +500,11 @@ struct WaveList {
 };
 
 // The grouped intermediate rows [n][F] and every slot's routing weight and
-// grouped row, for LDS (512 threads, n <= 8 MS): load() issues every load,
+// grouped row, for LDS (THREADS threads, n * 64 <= THREADS * MS): load() issues every load,
 // store() writes LDS once they have landed, so weight loads issued between the
 // two do not hold up the staging.  Past the end the last chunk is loaded and
 // stored again (the same value).
-template <int MS>
+template <int MS, int THREADS = 512>
 struct DownStage {
     uint4 c[MS];
     float w;
@@ -514,7 +514,7 @@ struct DownStage {
         const int n16 = n * VF * 2 / 16, tid = threadIdx.x;
         const uint4* g = reinterpret_cast<const uint4*>(abuf);
 #pragma unroll
-        for (int i = 0; i < MS; i++) c[i] = g[min(tid + i * 512, n16 - 1)];
+        for (int i = 0; i < MS; i++) c[i] = g[min(tid + i * THREADS, n16 - 1)];
         w = topk_w[min(tid, n - 1)];
         p = inv[min(tid, n - 1)];
     }
@@ -523,7 +523,7 @@ struct DownStage {
         const int n16 = n * VF * 2 / 16, tid = threadIdx.x;
         uint4* d = reinterpret_cast<uint4*>(as);
 #pragma unroll
-        for (int i = 0; i < MS; i++) d[min(tid + i * 512, n16 - 1)] = pair_order<QB>(c[i]);
+        for (int i = 0; i < MS; i++) d[min(tid + i * THREADS, n16 - 1)] = pair_order<QB>(c[i]);
         if (tid < n) {
             tw[tid] = w;
             tinv[tid] = p;
@@ -624,11 +624,15 @@ __global__ __launch_bounds__(512) void k_vdown(const uint16_t* __restrict__ abuf
 }
 
 // Block-quantised weights, F = 512: a wave covers four hidden rows (16 lanes
-// per row, a lane one quant block) and a quarter of the touched experts
-// (j = q, q + 4, ...); the block's 8 waves are 2 row groups x 4 quarters, so
-// a block owns 8 rows and combines them once all quarters are done.
+// per row, a lane one quant block) and an eighth of the touched experts
+// (j = q, q + 8, ...); the block's 16 waves are 2 row groups x 8 eighths, so
+// a block owns 8 rows and combines them once all eighths are done.  The
+// level decoding keeps this launch on the vector ALU, so it runs more waves
+// per CU (16, within 128 registers: at most two token rows per pass) with
+// one item's loads in flight each, rather than fewer waves with deep rings
+// of loads; the deeper rings also grow the unrolled code.
 template <int NT, int RING, int QB, int MS, int STEER>
-__global__ __launch_bounds__(512) void k_vdown_q(const uint16_t* __restrict__ abuf, const uint8_t* __restrict__ wd,
+__global__ __launch_bounds__(1024) void k_vdown_q(const uint16_t* __restrict__ abuf, const uint8_t* __restrict__ wd,
                                                  const uint16_t* __restrict__ sd, const int4* __restrict__ g_list,
                                                  const int32_t* __restrict__ g_nlist, const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ inv, int T, int K, int H,
@@ -644,45 +648,50 @@ __global__ __launch_bounds__(512) void k_vdown_q(const uint16_t* __restrict__ ab
     int* tinv = reinterpret_cast<int*>(tw + n);                        // [n]
     const int tid = threadIdx.x, wave = tid / WAVE, l = lane_id();
     const int nlist = __builtin_amdgcn_readfirstlane(*g_nlist);
-    const int rg = wave >> 2, q = wave & 3, g = l >> 4, b = l & 15;
+    const int rg = wave >> 3, q = wave & 7, g = l >> 4, b = l & 15;
     const int rloc = rg * 4 + g;                  // the lane's row within the block
     const int h = blockIdx.x * 8 + rloc;          // grid = H / 8: every row exists
     float* yr = ys + rloc * n;
-    const int n_items = nlist > q ? (nlist - q + 3) / 4 : 0;
+    const int n_items = nlist > q ? (nlist - q + 7) / 8 : 0;
     WaveList lst;
     lst.load(g_list, n);
-    DownStage<MS> stg;
+    DownStage<MS, 1024> stg;
     stg.load(abuf, n, topk_w, inv);
     constexpr int QW = QWords<QB>::n;
     struct Buf { uint32_t q[QW]; uint16_t d; };
     Buf wb[RING];
     auto load = [&](int i, Buf& bf) __attribute__((always_inline)) {
-        const long row = (long)lst.x(q + 4 * i) * H + h;
+        const long row = (long)lst.x(q + 8 * i) * H + h;
         load_block<QB>(bf.q, wd + row * (F * QB / 8), F, b);
         bf.d = ldnt_u16(sd + row * NB + b);
     };
     auto compute = [&](int i, const Buf& bf) __attribute__((always_inline)) {
-        const int j = q + 4 * i;
+        const int j = q + 8 * i;
         const int off = lst.y(j), nj = lst.z(j);
         const float d = fp16_to_f32(bf.d);
-        auto rows = [&](auto ntn) __attribute__((always_inline)) {
+        auto rows = [&](auto ntn, int t0) __attribute__((always_inline)) {
             constexpr int NTN = decltype(ntn)::value;
+            const int nr = nj - t0;
             float acc[NTN];
 #pragma unroll
             for (int t = 0; t < NTN; t++) {
                 acc[t] = 0.f;
-                if (t < nj) {
-                    const float S = asum[(off + t) * NB + b];
-                    const float D = dot_block_p<QB>(bf.q, as + (off + t) * F + b * 32);
+                if (t < nr) {
+                    const float S = asum[(off + t0 + t) * NB + b];
+                    const float D = dot_block_p<QB>(bf.q, as + (off + t0 + t) * F + b * 32);
                     acc[t] = d * fmaf(-zero_level<QB>(), S, D);
                 }
             }
             const float v = group16_tr_reduce<NTN>(acc);
             constexpr int shift = NTN == 16 ? 0 : NTN == 8 ? 1 : NTN == 4 ? 2 : NTN == 2 ? 3 : 4;
             const int t = b >> shift;
-            if ((b & ((1 << shift) - 1)) == 0 && t < nj) yr[off + t] = v;
+            if ((b & ((1 << shift) - 1)) == 0 && t < nr) yr[off + t0 + t] = v;
         };
-        by_rows<NT>(nj, rows);
+        if (nj <= VQ_ROWS) {
+            by_rows<(NT < VQ_ROWS ? NT : VQ_ROWS)>(nj, [&](auto ntn) __attribute__((always_inline)) { rows(ntn, 0); });
+        } else {
+            for (int t0 = 0; t0 < nj; t0 += VQ_ROWS) rows(std::integral_constant<int, VQ_ROWS>{}, t0);
+        }
     };
     if (n_items > 0) ring_start<RING>(0, 1, n_items, wb, load);
     stg.template store<QB>(as, tw, tinv, n);
@@ -721,7 +730,7 @@ __global__ __launch_bounds__(256) void k_vsteer(const float* __restrict__ hbuf, 
 namespace {
 constexpr int VG_FR = 2, VG_RING = 2;      // bf16 gate/up: 16 KB items, one in flight
 constexpr int VQ_FR = 2, VQ_RING = 3;      // quantised gate/up: 4 rows per item, two items in flight
-constexpr int VDQ_RING = 8;                // quantised down
+constexpr int VDQ_RING = 2;                // quantised down: one item in flight per wave, 16 waves per CU
 
 size_t gateup_lds(int T, int K, int quant) {
     const size_t n = (size_t)T * K;
@@ -798,7 +807,7 @@ hipError_t down_q_ms(hipStream_t st, const uint16_t* abuf, const void* wd, const
     static LdsLimit lim;
     hipError_t e = lim.ensure((const void*)kern, (int)VLDS_MAX);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(H / 8), dim3(512), down_lds(T, K, 1), st, abuf, (const uint8_t*)wd,
+    hipLaunchKernelGGL(kern, dim3(H / 8), dim3(1024), down_lds(T, K, 1), st, abuf, (const uint8_t*)wd,
                        (const uint16_t*)sd, o.list, o.nlist, o.w, o.inv, T, K, H, (const uint16_t*)residual,
                        (uint16_t*)out, hbuf);
     return hipSuccess;
@@ -806,8 +815,8 @@ hipError_t down_q_ms(hipStream_t st, const uint16_t* abuf, const void* wd, const
 template <int NT, int QB, int STEER>
 hipError_t down_q(hipStream_t st, const uint16_t* abuf, const void* wd, const void* sd, const VerifyOut& o, int T,
                   int K, int H, const void* residual, void* out, float* hbuf) {
-    return T * K <= 64 ? down_q_ms<NT, QB, 8, STEER>(st, abuf, wd, sd, o, T, K, H, residual, out, hbuf)
-                       : down_q_ms<NT, QB, 16, STEER>(st, abuf, wd, sd, o, T, K, H, residual, out, hbuf);
+    return T * K <= 64 ? down_q_ms<NT, QB, 4, STEER>(st, abuf, wd, sd, o, T, K, H, residual, out, hbuf)
+                       : down_q_ms<NT, QB, 8, STEER>(st, abuf, wd, sd, o, T, K, H, residual, out, hbuf);
 }
 
 template <int NT, int STEER>
