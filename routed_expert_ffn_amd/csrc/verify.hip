@@ -257,6 +257,7 @@ MOE_DEV void copy_to_lds(const void* __restrict__ src, void* __restrict__ dst, i
 }
 
 constexpr int VG_THREADS = 512;   // gate/up blocks: 8 waves, one token's selection each
+constexpr int VB_THREADS = 1024;  // bf16 gate/up: 16 waves (the first T select), items of one gate and one up row
 constexpr int VQ_ROWS = 2;        // token rows per pass of the quantised gate/up and down
 
 }  // namespace
@@ -266,7 +267,7 @@ constexpr int VQ_ROWS = 2;        // token rows per pass of the quantised gate/u
 // bf16 weights.  Item = (touched expert j, FR feature rows of gate and the
 // same FR of up) over all of H; lane l owns 8 consecutive inputs per 512.
 template <int NT, int FR, int RING, int VPL>
-__global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict__ lg, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(VB_THREADS) void k_vgateup(const float* __restrict__ lg, const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
                                                  int T, int K, int E, VerifyOut o, uint16_t* __restrict__ abuf) {
     constexpr int H = VH, CH = H / 512, F = VF;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
     const bool writer = blockIdx.x == 0;
     // the token rows' loads go out first, then wave t's loads of token t's
     // logits; x goes to LDS while the selection waits for the logits
-    XStage<NT, H, VG_THREADS> xst;
+    XStage<NT, H, VB_THREADS> xst;
     xst.load_x(x, T);
     uint32_t kv[VPL];
     load_order_keys<VPL>(lg + (long)min(wave, T - 1) * E, E, kv);
@@ -294,8 +295,8 @@ __global__ __launch_bounds__(VG_THREADS) void k_vgateup(const float* __restrict_
 
     const int tpe = F / FR;
     const int n_items = touched_count(touched, E) * tpe;
-    const int W = gridDim.x * (VG_THREADS / WAVE);
-    const int it = blockIdx.x * (VG_THREADS / WAVE) + wave;
+    const int W = gridDim.x * (VB_THREADS / WAVE);
+    const int it = blockIdx.x * (VB_THREADS / WAVE) + wave;
     const bool active = it < n_items;
 
     uint4 wbuf[RING][2 * FR][CH];
@@ -728,7 +729,7 @@ __global__ __launch_bounds__(256) void k_vsteer(const float* __restrict__ hbuf, 
 // ---------------------------------------------------------------------------- host
 
 namespace {
-constexpr int VG_FR = 2, VG_RING = 2;      // bf16 gate/up: 16 KB items, one in flight
+constexpr int VG_FR = 1, VG_RING = 2;      // bf16 gate/up: 8 KB items, one in flight per wave, 16 waves per CU
 constexpr int VQ_FR = 2, VQ_RING = 3;      // quantised gate/up: 4 rows per item, two items in flight
 constexpr int VDQ_RING = 2;                // quantised down: one item in flight per wave, 16 waves per CU
 
@@ -750,7 +751,7 @@ hipError_t gateup_bf16_v(int grid, hipStream_t st, const float* lg, const void* 
     static LdsLimit lim;
     hipError_t e = lim.ensure((const void*)kern, (int)VLDS_MAX);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(VG_THREADS), gateup_lds(T, K, 0), st, lg, (const uint16_t*)x,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(VB_THREADS), gateup_lds(T, K, 0), st, lg, (const uint16_t*)x,
                        (const uint16_t*)wg, (const uint16_t*)wu, T, K, E, o, abuf);
     return hipSuccess;
 }
