@@ -195,21 +195,29 @@ def bench_layer(torch, moe, synth, shape, cfg_id, steps, warmup, sets, use_graph
     acct = layer_bytes_and_flops(shape, counts, synth.expert_bytes(shape))
 
     fns = [(capture(torch, lambda L=L: step(L)).replay if use_graph else (lambda L=L: step(L))) for L in layers]
-    # consecutive steps run as one graph of the `sets` layer calls in rotation
+    # consecutive steps run as one graph of consecutive layer calls in rotation
     # order (as a model's consecutive layers would), so that a step does not
-    # carry a whole graph launch; a partial rotation replays single-call graphs
-    run_all = capture(torch, lambda: [step(L) for L in layers]).replay if use_graph and sets > 1 else None
+    # carry a whole graph launch: one graph per run of sets j .. j + m - 1
+    # (m up to the end of the rotation), captured beforehand, so that any step
+    # count replays as whole runs (a full rotation is the run from set 0)
+    runs = {}
+    if use_graph and sets > 1:
+        for j0 in range(sets):
+            for m in range(2, sets - j0 + 1):
+                runs[(j0, m)] = capture(torch, lambda j0=j0, m=m: [step(L) for L in layers[j0:j0 + m]]).replay
+    run_all = runs.get((0, sets))
 
     def run_steps(n, start):
         i = 0
         while i < n:
             j = (start + i) % sets
-            if run_all is not None and j == 0 and n - i >= sets:
-                run_all()
-                i += sets
+            m = min(sets - j, n - i)
+            if m > 1 and (j, m) in runs:
+                runs[(j, m)]()
             else:
+                m = 1
                 fns[j]()
-                i += 1
+            i += m
 
     timer = Timer(torch)
     if warmup > 0:
