@@ -730,7 +730,7 @@ __global__ __launch_bounds__(256) void k_vsteer(const float* __restrict__ hbuf, 
 
 namespace {
 constexpr int VG_FR = 1, VG_RING = 2;      // bf16 gate/up: 8 KB items, one in flight per wave, 16 waves per CU
-constexpr int VQ_FR = 2, VQ_RING = 3;      // quantised gate/up: 4 rows per item, two items in flight
+constexpr int VQ_FR = 2, VQ_RING = 2;      // quantised gate/up: 4 rows per item, one item in flight
 constexpr int VDQ_RING = 2;                // quantised down: one item in flight per wave, 16 waves per CU
 
 size_t gateup_lds(int T, int K, int quant) {
